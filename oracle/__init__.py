@@ -1,0 +1,145 @@
+"""Float64 CPU oracle of the fused vocabulary-softmax loss (ctypes loader).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg; never by the product path.  The arithmetic is
+in ``oracle.c``; this module only builds that file with gcc, loads it and
+marshals numpy arrays.
+
+Logits are numpy arrays ``[n][V]``: float32, or uint16 holding bf16 bit
+patterns.  Labels and ids are read as uint32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_c_double_p = ctypes.POINTER(ctypes.c_double)
+_c_i64_p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+           "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build()
+            lib = ctypes.CDLL(_LIB)
+            vp, i64, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
+            lib.oracle_row_lse.argtypes = [vp, ctypes.c_int, i64]
+            lib.oracle_row_lse.restype = dbl
+            lib.oracle_ce.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i64, i64,
+                                      i64, dbl, vp, vp, vp]
+            lib.oracle_ce.restype = None
+            lib.oracle_kl.argtypes = [vp, ctypes.c_int, vp, vp, i64, i64, i64, vp,
+                                      i64, i64, i64, dbl, vp, vp, vp]
+            lib.oracle_kl.restype = None
+            lib.oracle_topk.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp]
+            lib.oracle_topk.restype = None
+            lib.oracle_acc.argtypes = [vp, vp, i64, vp]
+            lib.oracle_acc.restype = None
+            _lib = lib
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError(f"oracle logits must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows2d(logits: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(logits)
+    if a.ndim == 1:
+        a = a.reshape(1, -1)
+    return a
+
+
+def _range_args(rng):
+    if rng is None:
+        return 0, 0, 0
+    seq_len, start, end = rng
+    return int(seq_len), int(start), int(end)
+
+
+def row_lse(row: np.ndarray) -> float:
+    a = np.ascontiguousarray(row).reshape(-1)
+    return _load().oracle_row_lse(_ptr(a), _dtype_code(a), a.size)
+
+
+def ce(logits, labels, rng=None, scale=1.0, row_index=None, want_grad=True):
+    """Per-row loss, lse and (optionally) the scaled gradient, all float64."""
+    a = _rows2d(logits)
+    n, V = a.shape
+    lab = np.ascontiguousarray(labels).astype(np.uint32, copy=False).reshape(-1)
+    assert lab.size == n
+    ridx = None if row_index is None else np.ascontiguousarray(row_index, dtype=np.int64)
+    loss = np.empty(n)
+    lse = np.empty(n)
+    grad = np.empty((n, V)) if want_grad else None
+    sl, st, en = _range_args(rng)
+    _load().oracle_ce(_ptr(a), _dtype_code(a), _ptr(lab), n, V, _ptr(ridx), sl, st, en,
+                      float(scale), _ptr(loss), _ptr(lse), _ptr(grad))
+    return loss, lse, grad
+
+
+def kl(logits, ids, probs, rng=None, coef=1.0, row_index=None, want_grad=True):
+    """Per-row KL, lse and (optionally) the scaled gradient, all float64."""
+    a = _rows2d(logits)
+    n, V = a.shape
+    idv = np.ascontiguousarray(ids).astype(np.uint32, copy=False).reshape(n, -1)
+    k = idv.shape[1]
+    pv = np.ascontiguousarray(probs, dtype=np.float32).reshape(n, k)
+    ridx = None if row_index is None else np.ascontiguousarray(row_index, dtype=np.int64)
+    loss = np.empty(n)
+    lse = np.empty(n)
+    grad = np.empty((n, V)) if want_grad else None
+    sl, st, en = _range_args(rng)
+    _load().oracle_kl(_ptr(a), _dtype_code(a), _ptr(idv), _ptr(pv), k, n, V, _ptr(ridx),
+                      sl, st, en, float(coef), _ptr(loss), _ptr(lse), _ptr(grad))
+    return loss, lse, grad
+
+
+def topk(logits, k):
+    """ids (uint32, [n][k], in output order) and float64 probs."""
+    a = _rows2d(logits)
+    n, V = a.shape
+    ids = np.empty((n, k), dtype=np.uint32)
+    probs = np.empty((n, k))
+    _load().oracle_topk(_ptr(a), _dtype_code(a), n, V, int(k), _ptr(ids), _ptr(probs))
+    return ids, probs
+
+
+def acc(dst, src):
+    """float32 dst + src, element-wise."""
+    d = np.ascontiguousarray(dst, dtype=np.float32).reshape(-1)
+    s = np.ascontiguousarray(src, dtype=np.float32).reshape(-1)
+    assert d.size == s.size
+    out = np.empty_like(d)
+    _load().oracle_acc(_ptr(d), _ptr(s), d.size, _ptr(out))
+    return out.reshape(np.shape(dst))
