@@ -1,0 +1,202 @@
+"""Throughput of the fused vocabulary-softmax loss path on one MI355X.
+
+One step is the whole path over one batch of 4096 token rows at V=32000
+(float32), inputs resident in HBM:
+  1. teacher top-k + renormalisation (k=64) of Zipf-shaped teacher logits;
+  2. distillation KL forward + in-place backward of a student batch against
+     that top-k (coef 1024/4096);
+  3. cross-entropy forward + in-place backward of an LM batch (8 sequences x
+     512 tokens, the first 128 tokens of each outside the loss, +6 at the
+     label on 30% of rows, scale 1/3072);
+  4. slice accumulate of two [4096][1024] float32 input gradients.
+The loss calls overwrite their logits with the gradient, so steps after the
+first run on the previous step's gradients; their cost does not depend on
+the values.
+
+Prints one JSON line.  `value` is logits rows per second of the whole step;
+`roofline` is for the step's dominant kernel, from HIP events recorded on
+the launch stream around every launch of the timed steps.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+
+NTOK, V, K_TOPK, HS = 4096, 32000, 64, 1024
+NSEQ, SEQ_LEN, PROMPT = 8, 512, 128
+
+
+def algorithmic_bytes():
+    """Bytes each kernel must move per launch (each input read once, each
+    output written once; see the design doc for the per-row figures)."""
+    row = V * 4
+    n_in = NSEQ * (SEQ_LEN - PROMPT)
+    return {
+        # top-k: read the row; write k ids and k probs
+        "topk": NTOK * row + NTOK * K_TOPK * 8,
+        # KL, row staged on chip: read + write the row; read ids and probs;
+        # write the loss
+        "kl": NTOK * 2 * row + NTOK * K_TOPK * 8 + NTOK * 4,
+        # CE: rows in the loss read + written, rows outside only written;
+        # labels read, loss written
+        "ce": n_in * 2 * row + (NTOK - n_in) * row + NTOK * 4 + NTOK * 4,
+        # slice accumulate: read dst and src, write dst
+        "acc": 3 * NTOK * HS * 4,
+    }
+
+
+def make_inputs(dev):
+    import torch
+    from gen import inputs as gi
+    teacher = gi.topk_zipf(dev, ntok=NTOK, V=V, k=K_TOPK)["teacher"]
+    kl_student = gi.normal_logits(NTOK, V, 2.0, 4001, dev)
+    ce = gi.ce_lm(dev, nseq=NSEQ, seq_len=SEQ_LEN, V=V, prompt=PROMPT)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4002)
+    dh0 = torch.randn((NTOK, HS), generator=g, device=dev)
+    dh1 = torch.randn((NTOK, HS), generator=g, device=dev)
+    return dict(teacher=teacher, kl_student=kl_student, ce_logits=ce["logits"],
+                labels=ce["labels"], rng=ce["rng"], scale=ce["scale"], dh0=dh0, dh1=dh1)
+
+
+def host_copies(x):
+    """Host bytes of the step's inputs, taken before the in-place calls."""
+    from gen.inputs import to_host_bytes
+    return {k: to_host_bytes(x[k]) for k in ("teacher", "kl_student", "ce_logits", "labels",
+                                              "dh0", "dh1")}
+
+
+def cpu_baseline(h, rng, scale, rows: int):
+    """The float64 oracle on the host over the first `rows` rows of the same
+    inputs, every stage of the step, wall-clock."""
+    import numpy as np
+    import oracle
+
+    oracle.topk(h["teacher"][:2], K_TOPK)  # load the library outside the timing
+    t0 = time.perf_counter()
+    ids, probs = oracle.topk(h["teacher"][:rows], K_TOPK)
+    oracle.kl(h["kl_student"][:rows], ids, probs.astype(np.float32), coef=1024.0 / NTOK)
+    oracle.ce(h["ce_logits"][:rows], h["labels"][:rows], rng=rng, scale=scale)
+    oracle.acc(h["dh0"][:rows], h["dh1"][:rows])
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of the {NTOK} rows of every stage (top-k, KL, CE, "
+                      f"slice accumulate) at V={V}, float64, {dt:.2f} s wall-clock"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=NTOK)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs on a single MI355X "
+              "(rows shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import vocab_softmax_loss_amd as vl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    x = make_inputs(dev)
+    host = None if args.no_cpu else host_copies(x)
+    ids = torch.empty((NTOK, K_TOPK), dtype=torch.int32, device=dev)
+    probs = torch.empty((NTOK, K_TOPK), device=dev)
+    kl_loss = torch.empty(NTOK, device=dev)
+    ce_loss = torch.empty(NTOK, device=dev)
+    coef = 1024.0 / NTOK
+    names = ["topk", "kl", "ce", "acc"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        vl.vl_topk_renorm(x["teacher"], K_TOPK, ids, probs)
+        mark(1)
+        vl.vl_kl_fwd_bwd(x["kl_student"], ids, probs, kl_loss, coef=coef)
+        mark(2)
+        vl.vl_ce_fwd_bwd(x["ce_logits"], x["labels"], ce_loss, rng=x["rng"], scale=x["scale"])
+        mark(3)
+        vl.vl_slice_acc(x["dh0"], x["dh1"])
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+              for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(events[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    per_kernel_ms = {n: sum(events[s][i].elapsed_time(events[s][i + 1])
+                            for s in range(args.steps)) / args.steps
+                     for i, n in enumerate(names)}
+
+    nbytes = algorithmic_bytes()
+    kernels = {}
+    for n in names:
+        gbs = nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9
+        kernels[n] = {"ms": round(per_kernel_ms[n], 5), "bytes": nbytes[n],
+                      "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "rows/s": round(NTOK / (per_kernel_ms[n] * 1e-3), 1)}
+    dom = max(names, key=lambda n: per_kernel_ms[n])
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB/s"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
+                "traffic": None}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(host, x["rng"], x["scale"], min(args.cpu_rows, NTOK))
+
+    out = {
+        "metric": "logits rows/s + achieved HBM GB/s (% of peak), fused CE/KL fwd+bwd at "
+                  "V=32000",
+        "value": round(NTOK / (ms_per_step * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "teacher top-k (k=64) + distillation KL fwd+bwd + CE fwd+bwd "
+                               "(8x512 tokens, prompt 128 masked) + slice accumulate, "
+                               "4096 rows x V=32000 float32",
+                   "ntok": NTOK, "V": V, "k": K_TOPK, "seq_len": SEQ_LEN,
+                   "loss_range": [PROMPT, SEQ_LEN], "slice_acc": [NTOK, HS]},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+/*
+ * vl.h -- C ABI of the fused row-wise vocabulary-softmax loss on AMD MI355X
+ * (gfx950).  Library: libvl.so.
+ *
+ * What it computes (the pages):
+ *   [CE] aprender-train 0.36.0, entrenar/autograd/wgpu_cross_entropy.rs:
+ *        module doc (loss = logsumexp(logits) - logits[label]; gradient
+ *        softmax - one_hot(label), written in place), CEForwardParams /
+ *        CEBackwardParams (loss range, scale), backward (scaled in-place
+ *        gradient), read_loss (mean over the loss range, taken by the caller).
+ *   [KL] cortiq-engine 0.8.21, src/gpu_wgpu/train_head.rs: module doc
+ *        (distillation KL against the teacher's renormalised top-k and its
+ *        gradient p_S - p_T, written in place and scaled), kl_rows, topk_rows
+ *        (teacher top-k with probabilities renormalised over the k), acc_add
+ *        (one vocabulary slice's input gradient added into another's).
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers owned by the caller.  The library keeps
+ *     no reference after the call returns and allocates no memory.
+ *   - Calls are asynchronous on `stream` (0 = the null stream of the current
+ *     device); the caller observes completion on that stream.
+ *   - Matrices are row-major and contiguous: row r of logits starts at
+ *     element r * V.  Buffers must not overlap, except that logits are both
+ *     input and output.
+ *   - Returns VL_OK (0) or a negative status; vl_strerror names it.  Invalid
+ *     sizes, dtypes and null pointers are rejected on the host before any
+ *     GPU work.  ntok == 0 (or n == 0) is a no-op that returns VL_OK.
+ *   - Preconditions NOT checked on the device: label < V; ids < V and
+ *     distinct within a row; probs >= 0; logits free of NaN and +inf with at
+ *     least one finite value per row.  Violating them never faults: a label
+ *     or id >= V makes that row's loss NaN and is skipped; duplicate ids
+ *     leave that gradient entry unspecified.
+ *   - Rows are 16-byte vectors when the logits pointer is 16-byte aligned
+ *     and V * element size is a multiple of 16; otherwise the same result is
+ *     computed one element at a time (slower).
+ */
+#ifndef VL_H
+#define VL_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of logits: IEEE float32, or bfloat16 (widened exactly to
+ * float32; stores round to nearest even). */
+typedef enum { VL_F32 = 0, VL_BF16 = 1 } vl_dtype;
+
+/* Loss range [CE: CEForwardParams / read_loss].  Row r takes part in the
+ * loss iff start <= r % seq_len < end; with seq_len == ntok this is one
+ * [loss_start, loss_end) range.  Requires 1 <= seq_len and
+ * 0 <= start <= end <= seq_len.  A NULL range means every row. */
+typedef struct {
+    int64_t seq_len;
+    int64_t start;
+    int64_t end;
+} vl_range;
+
+enum {
+    VL_OK = 0,
+    VL_EINVAL = -1,  /* bad size, range or null pointer */
+    VL_EDTYPE = -2,  /* unknown dtype */
+    VL_ELAUNCH = -3  /* the HIP runtime rejected the launch */
+};
+
+/*
+ * Fused cross-entropy forward + backward [CE: module doc, backward].
+ *   logits  [ntok][V] dtype, in: logits; out: gradient
+ *           scale * (softmax(row) - one_hot(label)), stored in dtype.
+ *   labels  [ntok] uint32, read only: the target id of each row (any causal
+ *           shift is the caller's).
+ *   loss    [ntok] float32, written: logsumexp(row) - row[label], unscaled.
+ *   lse     [ntok] float32 or NULL, written: logsumexp(row).
+ *   rng     loss range or NULL.  Rows outside it are not read; their loss
+ *           and lse are 0 and their gradient row is set to 0.
+ *   scale   gradient scale, e.g. 1 / (rows in the range) for the mean loss.
+ * Limits: 1 <= V <= 2^31 - 1, ntok >= 0.
+ */
+int vl_ce_fwd_bwd(void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
+                  int64_t ntok, int64_t V, const vl_range *rng, float scale,
+                  hipStream_t stream);
+
+/*
+ * Fused distillation KL forward + backward [KL: module doc, kl_rows].
+ *   logits  [ntok][V] dtype (student), in: logits; out: gradient
+ *           coef * (softmax(row) - t), t_j = probs[q] where ids[q] == j, else 0.
+ *   ids     [ntok][k] uint32, read only: the teacher's ids.
+ *   probs   [ntok][k] float32, read only: the teacher's probabilities, used
+ *           as given (no renormalisation).
+ *   loss    [ntok] float32, written: sum over q with probs[q] > 0 of
+ *           probs[q] * (ln probs[q] - row[ids[q]] + logsumexp(row)), unscaled.
+ *   lse, rng as for vl_ce_fwd_bwd.
+ *   coef    gradient scale, e.g. gscale / tokens of the step.
+ * Limits: 1 <= k <= V <= 2^19 (two bitmaps of V bits live in LDS).
+ */
+int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *probs, int64_t k,
+                  float *loss, float *lse, int64_t ntok, int64_t V, const vl_range *rng,
+                  float coef, hipStream_t stream);
+
+/*
+ * Teacher top-k with renormalised probabilities [KL: topk_rows].
+ *   logits  [ntok][V] dtype, read only.
+ *   ids     [ntok][k] uint32, written: the k ids first in the order (value
+ *           descending, id ascending); -0 and +0 tie.
+ *   probs   [ntok][k] float32, written: exp(v_q - v_0) / sum_{q<k} exp(v_q - v_0)
+ *           in the same order (the softmax restricted to the k).
+ * Limits: 1 <= k <= min(V, 2048), V <= 2^31 - 1.
+ */
+int vl_topk_renorm(const void *logits, int dtype, int64_t ntok, int64_t V, int64_t k,
+                   uint32_t *ids, float *probs, hipStream_t stream);
+
+/*
+ * Slice accumulate [KL: acc_add]: dst[i] = dst[i] + src[i] for i < n, the
+ * float32 sum rounded to nearest even (bit-exact).
+ *   dst [n] float32, read and written;  src [n] float32, read only.
+ */
+int vl_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream);
+
+/* Static text naming a status code. */
+const char *vl_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VL_H */

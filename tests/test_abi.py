@@ -1,0 +1,121 @@
+"""The C ABI on the CPU: libvl.so loads, exports every function include/vl.h
+declares, and rejects invalid arguments on the host before any GPU work.
+No call here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vl.h")
+
+VL_OK, VL_EINVAL, VL_EDTYPE, VL_ELAUNCH = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import vocab_softmax_loss_amd as vl
+    return vl._lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vl_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    assert declared_functions() == sorted(
+        ["vl_ce_fwd_bwd", "vl_kl_fwd_bwd", "vl_topk_renorm", "vl_slice_acc", "vl_strerror"])
+
+
+def test_library_exports_every_declared_function(lib):
+    raw = ctypes.CDLL(lib._name)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_strerror(lib):
+    for st in (VL_OK, VL_EINVAL, VL_EDTYPE, VL_ELAUNCH, 7):
+        assert lib.vl_strerror(st)
+    assert lib.vl_strerror(VL_EDTYPE) != lib.vl_strerror(VL_EINVAL)
+
+
+# A non-null pointer that is never dereferenced: every call below fails its
+# host checks (or is a no-op) before touching it.
+P = ctypes.c_void_p(0x1000)
+
+
+def ce(lib, **kw):
+    a = dict(logits=P, dtype=0, labels=P, loss=P, lse=None, ntok=4, V=10, rng=None,
+             scale=1.0, stream=None)
+    a.update(kw)
+    return lib.vl_ce_fwd_bwd(a["logits"], a["dtype"], a["labels"], a["loss"], a["lse"],
+                             a["ntok"], a["V"], a["rng"], a["scale"], a["stream"])
+
+
+def kl(lib, **kw):
+    a = dict(logits=P, dtype=0, ids=P, probs=P, k=2, loss=P, lse=None, ntok=4, V=10,
+             rng=None, coef=1.0, stream=None)
+    a.update(kw)
+    return lib.vl_kl_fwd_bwd(a["logits"], a["dtype"], a["ids"], a["probs"], a["k"],
+                             a["loss"], a["lse"], a["ntok"], a["V"], a["rng"], a["coef"],
+                             a["stream"])
+
+
+def rng(seq_len, start, end):
+    import vocab_softmax_loss_amd as vl
+    return ctypes.byref(vl.vl_range(seq_len, start, end))
+
+
+def test_ce_host_checks(lib):
+    assert ce(lib, dtype=2) == VL_EDTYPE
+    assert ce(lib, dtype=-1) == VL_EDTYPE
+    assert ce(lib, V=0) == VL_EINVAL
+    assert ce(lib, V=1 << 31) == VL_EINVAL
+    assert ce(lib, ntok=-1) == VL_EINVAL
+    assert ce(lib, ntok=1 << 62, V=1 << 20) == VL_EINVAL  # ntok*V overflows
+    assert ce(lib, logits=None) == VL_EINVAL
+    assert ce(lib, labels=None) == VL_EINVAL
+    assert ce(lib, loss=None) == VL_EINVAL
+    assert ce(lib, rng=rng(0, 0, 0)) == VL_EINVAL
+    assert ce(lib, rng=rng(8, 5, 4)) == VL_EINVAL
+    assert ce(lib, rng=rng(8, -1, 4)) == VL_EINVAL
+    assert ce(lib, rng=rng(8, 0, 9)) == VL_EINVAL
+    # ntok == 0 is a no-op, even with null pointers
+    assert ce(lib, ntok=0, logits=None, labels=None, loss=None) == VL_OK
+
+
+def test_kl_host_checks(lib):
+    assert kl(lib, dtype=3) == VL_EDTYPE
+    assert kl(lib, k=0) == VL_EINVAL
+    assert kl(lib, k=11) == VL_EINVAL  # k > V
+    assert kl(lib, V=(1 << 19) + 1, k=4) == VL_EINVAL  # two V-bit bitmaps exceed LDS
+    assert kl(lib, ids=None) == VL_EINVAL
+    assert kl(lib, probs=None) == VL_EINVAL
+    assert kl(lib, loss=None) == VL_EINVAL
+    assert kl(lib, rng=rng(4, 3, 2)) == VL_EINVAL
+    assert kl(lib, ntok=0, logits=None) == VL_OK
+
+
+def test_topk_host_checks(lib):
+    f = lib.vl_topk_renorm
+    assert f(P, 9, 4, 10, 2, P, P, None) == VL_EDTYPE
+    assert f(P, 0, 4, 10, 0, P, P, None) == VL_EINVAL
+    assert f(P, 0, 4, 10, 11, P, P, None) == VL_EINVAL  # k > V
+    assert f(P, 0, 4, 5000, 2049, P, P, None) == VL_EINVAL  # k > 2048
+    assert f(P, 0, 4, 0, 1, P, P, None) == VL_EINVAL
+    assert f(P, 0, -1, 10, 2, P, P, None) == VL_EINVAL
+    assert f(None, 0, 4, 10, 2, P, P, None) == VL_EINVAL
+    assert f(P, 0, 4, 10, 2, None, P, None) == VL_EINVAL
+    assert f(P, 0, 4, 10, 2, P, None, None) == VL_EINVAL
+    assert f(None, 1, 0, 10, 2, None, None, None) == VL_OK
+
+
+def test_slice_acc_host_checks(lib):
+    f = lib.vl_slice_acc
+    assert f(P, P, -1, None) == VL_EINVAL
+    assert f(None, P, 4, None) == VL_EINVAL
+    assert f(P, None, 4, None) == VL_EINVAL
+    assert f(None, None, 0, None) == VL_OK

@@ -1,0 +1,141 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (the same C-ABI calls on the same shapes).  Every row where the oracle
+finishes in seconds (the 4096 x 32000 workloads), sampled rows plus
+whole-tensor invariants for the 4-5 GB ones.  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gen import inputs as gi
+from gen.inputs import to_host_bytes
+from tests.parity import bf16_bits_to_f64, check_grad, check_loss, check_topk
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def vl():
+    import vocab_softmax_loss_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def sample(ntok, n, seed, extra=()):
+    r = np.random.default_rng(seed).choice(ntok, size=n, replace=False)
+    return np.unique(np.concatenate([r, np.asarray(extra, dtype=np.int64)]))
+
+
+def topk_invariants(x, ids, probs, k):
+    """Whole-tensor checks valid at any size: ids distinct and in range,
+    values non-increasing with ascending ids among equal values, probs
+    positive-or-zero, non-increasing and summing to 1."""
+    ids_l = ids.long()
+    assert int(ids_l.min()) >= 0 and int(ids_l.max()) < x.shape[1]
+    s = ids_l.sort(dim=1).values
+    assert bool((s[:, 1:] != s[:, :-1]).all()), "repeated id in a row"
+    v = x.gather(1, ids_l).float()
+    dv = v[:, 1:] - v[:, :-1]
+    assert bool((dv <= 0).all()), "values not non-increasing"
+    tie = dv == 0
+    assert bool(((ids_l[:, 1:] > ids_l[:, :-1]) | ~tie).all()), "tie not in id order"
+    assert bool((probs >= 0).all())
+    assert bool((probs[:, 1:] <= probs[:, :-1] * (1 + 1e-6)).all())
+    assert float((probs.double().sum(dim=1) - 1).abs().max()) < 1e-5
+
+
+def test_ce_lm_full(vl):
+    """Cross-entropy, 8 x 512 tokens, V=32000, prompt mask: every row."""
+    c = gi.ce_lm(DEV)
+    x, lab, rng, scale = c["logits"], c["labels"], c["rng"], c["scale"]
+    host = to_host_bytes(x)
+    labh = lab.cpu().numpy()
+    loss = torch.empty(x.shape[0], device=DEV)
+    lse = torch.empty(x.shape[0], device=DEV)
+    vl.vl_ce_fwd_bwd(x, lab, loss, lse, rng=rng, scale=scale)
+    torch.cuda.synchronize()
+    loss, lse = loss.cpu().numpy(), lse.cpu().numpy()
+    for r0 in range(0, x.shape[0], 512):
+        r1 = r0 + 512
+        ol, olse, og = oracle.ce(host[r0:r1], labh[r0:r1], rng=rng, scale=scale,
+                                 row_index=np.arange(r0, r1))
+        check_loss(loss[r0:r1], ol, "f32")
+        check_loss(lse[r0:r1], olse, "f32", "lse")
+        check_grad(x[r0:r1].cpu().numpy(), og, "f32", scale)
+
+
+def test_topk_zipf_full(vl):
+    """Teacher top-k, 4096 x 32000, k=64: every row."""
+    c = gi.topk_zipf(DEV)
+    t, k = c["teacher"], c["k"]
+    ids = torch.empty((t.shape[0], k), dtype=torch.int32, device=DEV)
+    probs = torch.empty((t.shape[0], k), device=DEV)
+    vl.vl_topk_renorm(t, k, ids, probs)
+    torch.cuda.synchronize()
+    topk_invariants(t, ids, probs, k)
+    oi, op = oracle.topk(to_host_bytes(t), k)
+    check_topk(ids.cpu().numpy().view(np.uint32), probs.cpu().numpy(), oi, op)
+
+
+def test_kl_large_full(vl):
+    """Distillation KL, 8192 x 128256 float32, k=128: sampled rows through
+    the oracle (loss on 512 rows, gradient on 24)."""
+    c = gi.kl_large(DEV)
+    x, ids, probs, coef = c["logits"], c["ids"], c["probs"], c["coef"]
+    rows = sample(x.shape[0], 512, 41, extra=[0, x.shape[0] - 1])
+    host = to_host_bytes(x[torch.from_numpy(rows).to(DEV)])
+    idh = ids.cpu().numpy()[rows]
+    ph = probs.cpu().numpy()[rows]
+    loss = torch.empty(x.shape[0], device=DEV)
+    lse = torch.empty(x.shape[0], device=DEV)
+    vl.vl_kl_fwd_bwd(x, ids, probs, loss, lse, coef=coef)
+    torch.cuda.synchronize()
+    ol, olse, _ = oracle.kl(host, idh, ph, coef=coef, want_grad=False)
+    check_loss(loss.cpu().numpy()[rows], ol, "f32")
+    check_loss(lse.cpu().numpy()[rows], olse, "f32", "lse")
+    g_rows = rows[:: max(1, len(rows) // 24)]
+    sel = np.searchsorted(rows, g_rows)
+    _, _, og = oracle.kl(host[sel], idh[sel], ph[sel], coef=coef)
+    check_grad(x[torch.from_numpy(g_rows).to(DEV)].cpu().numpy(), og, "f32", coef)
+    # every row: gradient rows sum to coef * (1 - sum p), finite losses
+    gs = x.sum(dim=1, dtype=torch.float64)
+    want = coef * (1.0 - probs.sum(dim=1, dtype=torch.float64))
+    assert float((gs - want).abs().max()) < 1e-4
+    assert bool(torch.isfinite(loss).all())
+
+
+def test_kl_bf16_sliced_full(vl):
+    """bf16 distillation at V=151936: teacher top-k (k=256) by the GPU, KL of
+    the student against it, and the slice accumulate of two [16384][1024]
+    float32 input gradients.  End to end against the oracle's own top-k on
+    sampled rows; ids bit-exact on the sampled rows and invariants on all."""
+    c = gi.kl_bf16_sliced(DEV)
+    x, t, k, coef = c["logits"], c["teacher"], c["k"], c["coef"]
+    ntok = x.shape[0]
+    rows = sample(ntok, 24, 51, extra=[0, ntok - 1])
+    rows_t = torch.from_numpy(rows).to(DEV)
+    th = to_host_bytes(t[rows_t])
+    xh = to_host_bytes(x[rows_t])
+
+    ids = torch.empty((ntok, k), dtype=torch.int32, device=DEV)
+    probs = torch.empty((ntok, k), device=DEV)
+    vl.vl_topk_renorm(t, k, ids, probs)
+    torch.cuda.synchronize()
+    topk_invariants(t, ids, probs, k)
+    oi, op = oracle.topk(th, k)
+    check_topk(ids[rows_t].cpu().numpy().view(np.uint32), probs[rows_t].cpu().numpy(), oi, op)
+
+    loss = torch.empty(ntok, device=DEV)
+    vl.vl_kl_fwd_bwd(x, ids, probs, loss, coef=coef)
+    torch.cuda.synchronize()
+    ol, _, og = oracle.kl(xh, oi, op.astype(np.float32), coef=coef)
+    check_loss(loss.cpu().numpy()[rows], ol, "bf16")
+    check_grad(to_host_bytes(x[rows_t]), og, "bf16", coef)
+
+    d0, d1 = c["dh0"], c["dh1"]
+    want = oracle.acc(d0.cpu().numpy(), d1.cpu().numpy())
+    vl.vl_slice_acc(d0, d1)
+    torch.cuda.synchronize()
+    assert np.array_equal(d0.cpu().numpy().view(np.uint32), want.view(np.uint32))

@@ -1,0 +1,164 @@
+"""Python binding of libvl.so, the fused vocabulary-softmax loss for MI355X.
+
+The functions carry the C ABI's names and arguments (include/vl.h).  They only
+marshal arguments: check that tensors are contiguous device tensors of the
+right dtype and shape, pass their device pointers and the current HIP stream,
+and raise on a non-zero status.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback.  Importing this module fails
+loudly when libvl.so has not been built.
+
+Tensors:
+  logits  [ntok][V] torch.float32 or torch.bfloat16 (in place for the losses)
+  labels  [ntok], ids [ntok][k]: torch.int32 or torch.uint32 (read as uint32)
+  probs   [ntok][k] torch.float32
+  loss, lse [ntok] torch.float32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "VL_F32", "VL_BF16", "VLError", "lib_path",
+    "vl_ce_fwd_bwd", "vl_kl_fwd_bwd", "vl_topk_renorm", "vl_slice_acc", "vl_strerror",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libvl.so")
+
+VL_F32 = 0
+VL_BF16 = 1
+
+
+class VLError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {vl_strerror(status)} (status {status})")
+        self.status = status
+
+
+class vl_range(ctypes.Structure):
+    _fields_ = [("seq_len", ctypes.c_int64), ("start", ctypes.c_int64),
+                ("end", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with "
+            "`python -m vocab_softmax_loss_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    rp = ctypes.POINTER(vl_range)
+    lib.vl_ce_fwd_bwd.argtypes = [vp, i32, vp, vp, vp, i64, i64, rp, f32, vp]
+    lib.vl_kl_fwd_bwd.argtypes = [vp, i32, vp, vp, i64, vp, vp, i64, i64, rp, f32, vp]
+    lib.vl_topk_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    lib.vl_slice_acc.argtypes = [vp, vp, i64, vp]
+    lib.vl_strerror.argtypes = [i32]
+    lib.vl_strerror.restype = ctypes.c_char_p
+    for f in (lib.vl_ce_fwd_bwd, lib.vl_kl_fwd_bwd, lib.vl_topk_renorm, lib.vl_slice_acc):
+        f.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def vl_strerror(status: int) -> str:
+    return _lib.vl_strerror(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return VL_F32
+    if t.dtype == torch.bfloat16:
+        return VL_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+_INT_IDS = (torch.int32, torch.uint32)
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream)
+
+
+def _range(rng):
+    if rng is None:
+        return None
+    r = vl_range(*[int(v) for v in rng])
+    return ctypes.byref(r)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise VLError(status, where)
+
+
+def vl_ce_fwd_bwd(logits, labels, loss, lse=None, rng=None, scale=1.0, stream=None):
+    """Fused CE forward + in-place backward; see vl_ce_fwd_bwd in vl.h.
+    ``rng`` is (seq_len, start, end) or None."""
+    ntok, V = logits.shape
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_ce_fwd_bwd(
+            _dev(logits, "logits", None), _dtype_code(logits),
+            _dev(labels, "labels", _INT_IDS, (ntok,)),
+            _dev(loss, "loss", (torch.float32,), (ntok,)),
+            None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, V, _range(rng), float(scale), _stream(logits, stream)), "vl_ce_fwd_bwd")
+
+
+def vl_kl_fwd_bwd(logits, ids, probs, loss, lse=None, rng=None, coef=1.0, stream=None):
+    """Fused distillation KL forward + in-place backward; see vl_kl_fwd_bwd."""
+    ntok, V = logits.shape
+    k = ids.shape[1] if ids.dim() == 2 else 0
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_kl_fwd_bwd(
+            _dev(logits, "logits", None), _dtype_code(logits),
+            _dev(ids, "ids", _INT_IDS, (ntok, k)),
+            _dev(probs, "probs", (torch.float32,), (ntok, k)), k,
+            _dev(loss, "loss", (torch.float32,), (ntok,)),
+            None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, V, _range(rng), float(coef), _stream(logits, stream)), "vl_kl_fwd_bwd")
+
+
+def vl_topk_renorm(logits, k, ids, probs, stream=None):
+    """Teacher top-k ids and renormalised probabilities; see vl_topk_renorm."""
+    ntok, V = logits.shape
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_topk_renorm(
+            _dev(logits, "logits", None), _dtype_code(logits), ntok, V, int(k),
+            _dev(ids, "ids", _INT_IDS, (ntok, k)),
+            _dev(probs, "probs", (torch.float32,), (ntok, k)),
+            _stream(logits, stream)), "vl_topk_renorm")
+
+
+def vl_slice_acc(dst, src, stream=None):
+    """dst += src (float32, bit-exact); see vl_slice_acc."""
+    n = dst.numel()
+    with torch.cuda.device(dst.device):
+        _check(_lib.vl_slice_acc(
+            _dev(dst, "dst", (torch.float32,)),
+            _dev(src, "src", (torch.float32,), tuple(dst.shape)), n,
+            _stream(dst, stream)), "vl_slice_acc")

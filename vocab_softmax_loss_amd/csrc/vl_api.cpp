@@ -1,0 +1,163 @@
+// C ABI of libvl.so (declared in include/vl.h): host-side argument checks,
+// then one asynchronous launch on the caller's stream.  No allocation, no
+// synchronisation, no retained pointers.
+#include "vl.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "vl_launch.hpp"
+
+namespace vl {
+
+int device_cus()
+{
+    static std::mutex mu;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+}  // namespace vl
+
+namespace {
+
+constexpr int64_t kMaxV = (int64_t(1) << 31) - 1;
+
+bool bad_dtype(int dtype) { return dtype != VL_F32 && dtype != VL_BF16; }
+
+// Shared checks of the two loss calls; fills the range fields of `a`.
+int check_rows(int dtype, int64_t ntok, int64_t V, const vl_range *rng, vl::RowArgs &a)
+{
+    if (bad_dtype(dtype))
+        return VL_EDTYPE;
+    if (ntok < 0 || V < 1 || V > kMaxV)
+        return VL_EINVAL;
+    if (ntok > INT64_MAX / V)
+        return VL_EINVAL;
+    if (rng) {
+        if (rng->seq_len < 1 || rng->start < 0 || rng->start > rng->end ||
+            rng->end > rng->seq_len)
+            return VL_EINVAL;
+        a.seq_len = rng->seq_len;
+        a.start = rng->start;
+        a.end = rng->end;
+    } else {
+        a.seq_len = 0;
+        a.start = 0;
+        a.end = 0;
+    }
+    a.ntok = ntok;
+    a.V = V;
+    return VL_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? VL_OK : VL_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int vl_ce_fwd_bwd(void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
+                  int64_t ntok, int64_t V, const vl_range *rng, float scale,
+                  hipStream_t stream)
+{
+    vl::RowArgs a{};
+    int st = check_rows(dtype, ntok, V, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (ntok == 0)
+        return VL_OK;
+    if (!logits || !labels || !loss)
+        return VL_EINVAL;
+    a.logits = logits;
+    a.labels = labels;
+    a.loss = loss;
+    a.lse = lse;
+    a.k = 1;
+    a.coef = scale;
+    return status_of(vl::launch_rows(dtype, false, a, stream));
+}
+
+int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *probs, int64_t k,
+                  float *loss, float *lse, int64_t ntok, int64_t V, const vl_range *rng,
+                  float coef, hipStream_t stream)
+{
+    vl::RowArgs a{};
+    int st = check_rows(dtype, ntok, V, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (V > vl::kMaxKlVocab || k < 1 || k > V)
+        return VL_EINVAL;
+    if (ntok > INT64_MAX / k)
+        return VL_EINVAL;
+    if (ntok == 0)
+        return VL_OK;
+    if (!logits || !ids || !probs || !loss)
+        return VL_EINVAL;
+    a.logits = logits;
+    a.ids = ids;
+    a.probs = probs;
+    a.loss = loss;
+    a.lse = lse;
+    a.k = k;
+    a.coef = coef;
+    return status_of(vl::launch_rows(dtype, true, a, stream));
+}
+
+int vl_topk_renorm(const void *logits, int dtype, int64_t ntok, int64_t V, int64_t k,
+                   uint32_t *ids, float *probs, hipStream_t stream)
+{
+    if (bad_dtype(dtype))
+        return VL_EDTYPE;
+    if (ntok < 0 || V < 1 || V > kMaxV || k < 1 || k > V || k > vl::kMaxTopk)
+        return VL_EINVAL;
+    if (ntok > INT64_MAX / V)
+        return VL_EINVAL;
+    if (ntok == 0)
+        return VL_OK;
+    if (!logits || !ids || !probs)
+        return VL_EINVAL;
+    vl::TopkArgs a{logits, ntok, V, k, ids, probs};
+    return status_of(vl::launch_topk(dtype, a, stream));
+}
+
+int vl_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream)
+{
+    if (n < 0)
+        return VL_EINVAL;
+    if (n == 0)
+        return VL_OK;
+    if (!dst || !src)
+        return VL_EINVAL;
+    return status_of(vl::launch_slice_acc(dst, src, n, stream));
+}
+
+const char *vl_strerror(int status)
+{
+    switch (status) {
+    case VL_OK:
+        return "ok";
+    case VL_EINVAL:
+        return "invalid argument (size, range, k or null pointer)";
+    case VL_EDTYPE:
+        return "unknown dtype (expected VL_F32 or VL_BF16)";
+    case VL_ELAUNCH:
+        return "the HIP runtime rejected the kernel launch";
+    default:
+        return "unknown status";
+    }
+}
+
+}  // extern "C"
