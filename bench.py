@@ -18,6 +18,10 @@ Prints one JSON line.  `value` is logits rows per second of the whole step;
 the launch stream around every launch of the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+                    [--workload step|ce_lm|topk_zipf|kl_large|kl_bf16]
+
+The other workloads time one configuration each at its full size (for the
+per-kernel rooflines in the design doc); the default line is the step above.
 """
 from __future__ import annotations
 
@@ -95,6 +99,97 @@ def cpu_baseline(h, rng, scale, rows: int):
                       f"slice accumulate) at V={V}, float64, {dt:.2f} s wall-clock"}
 
 
+def other_workload(name, dev):
+    """(calls, bytes per call, ntok, config) of one full-size configuration.
+    Each call is (kernel name, function)."""
+    import torch
+    import vocab_softmax_loss_amd as vl
+    from gen import inputs as gi
+
+    if name == "ce_lm":
+        c = gi.ce_lm(dev)
+        ntok, V = c["logits"].shape
+        loss = torch.empty(ntok, device=dev)
+        n_in = 8 * 384
+        calls = [("ce", lambda: vl.vl_ce_fwd_bwd(c["logits"], c["labels"], loss, rng=c["rng"],
+                                                 scale=c["scale"]))]
+        nbytes = {"ce": n_in * 2 * V * 4 + (ntok - n_in) * V * 4 + ntok * 8}
+        cfg = {"workload": gi.CE_LM.name, "ntok": ntok, "V": V, "dtype": "f32"}
+    elif name == "topk_zipf":
+        c = gi.topk_zipf(dev)
+        t, k = c["teacher"], c["k"]
+        ntok, V = t.shape
+        ids = torch.empty((ntok, k), dtype=torch.int32, device=dev)
+        probs = torch.empty((ntok, k), device=dev)
+        calls = [("topk", lambda: vl.vl_topk_renorm(t, k, ids, probs))]
+        nbytes = {"topk": ntok * V * 4 + ntok * k * 8}
+        cfg = {"workload": gi.TOPK_ZIPF.name, "ntok": ntok, "V": V, "k": k, "dtype": "f32"}
+    elif name == "kl_large":
+        c = gi.kl_large(dev)
+        x = c["logits"]
+        ntok, V = x.shape
+        k = c["ids"].shape[1]
+        loss = torch.empty(ntok, device=dev)
+        calls = [("kl", lambda: vl.vl_kl_fwd_bwd(x, c["ids"], c["probs"], loss, coef=c["coef"]))]
+        # online variant: the row is read twice and written once
+        nbytes = {"kl": ntok * 3 * V * 4 + ntok * k * 8 + ntok * 4}
+        cfg = {"workload": gi.KL_LARGE.name, "ntok": ntok, "V": V, "k": k, "dtype": "f32",
+               "bytes_model": "2R+1W"}
+    elif name == "kl_bf16":
+        c = gi.kl_bf16_sliced(dev)
+        x, t, k = c["logits"], c["teacher"], c["k"]
+        ntok, V = x.shape
+        hs = c["dh0"].shape[1]
+        ids = torch.empty((ntok, k), dtype=torch.int32, device=dev)
+        probs = torch.empty((ntok, k), device=dev)
+        loss = torch.empty(ntok, device=dev)
+        calls = [("topk", lambda: vl.vl_topk_renorm(t, k, ids, probs)),
+                 ("kl", lambda: vl.vl_kl_fwd_bwd(x, ids, probs, loss, coef=c["coef"])),
+                 ("acc", lambda: vl.vl_slice_acc(c["dh0"], c["dh1"]))]
+        nbytes = {"topk": ntok * V * 2 + ntok * k * 8,
+                  "kl": ntok * 3 * V * 2 + ntok * k * 8 + ntok * 4,
+                  "acc": 3 * ntok * hs * 4}
+        cfg = {"workload": gi.KL_BF16.name, "ntok": ntok, "V": V, "k": k, "dtype": "bf16",
+               "bytes_model": "KL 2R+1W"}
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return calls, nbytes, ntok, cfg
+
+
+def time_calls(calls, steps, warmup):
+    """Average ms per call (HIP events on the current stream around every
+    launch) and per sequence of all calls."""
+    import torch
+    for _ in range(warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    n = len(calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(steps):
+        for i, (_, fn) in enumerate(calls):
+            ev[s][i].record()
+            fn()
+        ev[s][n].record()
+    t1.record()
+    torch.cuda.synchronize()
+    per = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+           for i, (name, _) in enumerate(calls)}
+    return per, t0.elapsed_time(t1) / steps
+
+
+def kernel_table(per_ms, nbytes, ntok):
+    out = {}
+    for n, ms in per_ms.items():
+        gbs = nbytes[n] / (ms * 1e-3) / 1e9
+        out[n] = {"ms": round(ms, 5), "bytes": nbytes[n], "GB/s": round(gbs, 1),
+                  "frac": round(gbs / HBM_PEAK_GBS, 4), "rows/s": round(ntok / (ms * 1e-3), 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +197,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=NTOK)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", default="step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs on a single MI355X "
@@ -113,6 +209,22 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.workload != "step":
+        calls, nbytes, ntok, cfg = other_workload(args.workload, dev)
+        per, seq_ms = time_calls(calls, args.steps, args.warmup)
+        kernels = kernel_table(per, nbytes, ntok)
+        dom = max(per, key=per.get)
+        print(json.dumps({
+            "metric": f"rows/s and achieved HBM GB/s of one configuration ({args.workload})",
+            "value": round(ntok / (seq_ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(seq_ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": cfg["dtype"], "data": "synthetic", "config": cfg,
+            "roofline": {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB/s"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
+                         "traffic": None},
+            "kernels": kernels, "cpu_baseline": None}), flush=True)
+        return
     x = make_inputs(dev)
     host = None if args.no_cpu else host_copies(x)
     ids = torch.empty((NTOK, K_TOPK), dtype=torch.int32, device=dev)
@@ -120,50 +232,16 @@ def main():
     kl_loss = torch.empty(NTOK, device=dev)
     ce_loss = torch.empty(NTOK, device=dev)
     coef = 1024.0 / NTOK
-    names = ["topk", "kl", "ce", "acc"]
-
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record()
-        mark(0)
-        vl.vl_topk_renorm(x["teacher"], K_TOPK, ids, probs)
-        mark(1)
-        vl.vl_kl_fwd_bwd(x["kl_student"], ids, probs, kl_loss, coef=coef)
-        mark(2)
-        vl.vl_ce_fwd_bwd(x["ce_logits"], x["labels"], ce_loss, rng=x["rng"], scale=x["scale"])
-        mark(3)
-        vl.vl_slice_acc(x["dh0"], x["dh1"])
-        mark(4)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
-              for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for s in range(args.steps):
-        step(events[s])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    per_kernel_ms = {n: sum(events[s][i].elapsed_time(events[s][i + 1])
-                            for s in range(args.steps)) / args.steps
-                     for i, n in enumerate(names)}
-
-    nbytes = algorithmic_bytes()
-    kernels = {}
-    for n in names:
-        gbs = nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9
-        kernels[n] = {"ms": round(per_kernel_ms[n], 5), "bytes": nbytes[n],
-                      "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                      "rows/s": round(NTOK / (per_kernel_ms[n] * 1e-3), 1)}
-    dom = max(names, key=lambda n: per_kernel_ms[n])
+    calls = [
+        ("topk", lambda: vl.vl_topk_renorm(x["teacher"], K_TOPK, ids, probs)),
+        ("kl", lambda: vl.vl_kl_fwd_bwd(x["kl_student"], ids, probs, kl_loss, coef=coef)),
+        ("ce", lambda: vl.vl_ce_fwd_bwd(x["ce_logits"], x["labels"], ce_loss, rng=x["rng"],
+                                        scale=x["scale"])),
+        ("acc", lambda: vl.vl_slice_acc(x["dh0"], x["dh1"])),
+    ]
+    per_kernel_ms, ms_per_step = time_calls(calls, args.steps, args.warmup)
+    kernels = kernel_table(per_kernel_ms, algorithmic_bytes(), NTOK)
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB/s"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
                 "traffic": None}

@@ -50,13 +50,9 @@ int check_rows(int dtype, int64_t ntok, int64_t V, const vl_range *rng, vl::RowA
         if (rng->seq_len < 1 || rng->start < 0 || rng->start > rng->end ||
             rng->end > rng->seq_len)
             return VL_EINVAL;
-        a.seq_len = rng->seq_len;
-        a.start = rng->start;
-        a.end = rng->end;
+        a.walk = vl::make_walk(ntok, rng->seq_len, rng->start, rng->end);
     } else {
-        a.seq_len = 0;
-        a.start = 0;
-        a.end = 0;
+        a.walk = vl::make_walk(ntok, 0, 0, 0);
     }
     a.ntok = ntok;
     a.V = V;

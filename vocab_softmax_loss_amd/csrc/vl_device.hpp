@@ -68,6 +68,52 @@ __device__ __forceinline__ int lanes_below(uint64_t mask)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
 }
 
+// Workgroup barrier for data exchanged through LDS.  It waits only for this
+// wave's own LDS operations (lgkmcnt(0)) and then s_barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+// __syncthreads(), and even an LDS-scoped fence, would also wait for all of
+// the wave's outstanding HBM loads and stores -- including asynchronous
+// loads into LDS slots that no other wave reads -- and so wait for a
+// prefetch at every barrier.
+__device__ __forceinline__ void block_sync_lds()
+{
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
+
+// Asynchronous 16-byte load from global memory into LDS
+// (global_load_lds_dwordx4): lane l of the wave writes lds_base + 16 l,
+// where lds_base must be the same for the whole wave.  Completion is counted
+// by vmcnt only; the compiler does not order later LDS reads after it, so
+// callers wait explicitly (wait_vm_all) before reading the destination and
+// wait for their own earlier reads of it (wait_lds_all) before issuing.
+__device__ __forceinline__ void load_to_lds16(const void *gptr, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base,
+                                     16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every vector memory operation of this wave is done.
+// Encoding (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8];
+// expcnt and lgkmcnt left at their maxima (no wait on them).
+__device__ __forceinline__ void wait_vm_all()
+{
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __asm__ __volatile__("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS (and scalar memory) operations are
+// done.
+__device__ __forceinline__ void wait_lds_all()
+{
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __asm__ __volatile__("" ::: "memory");
+}
+
 // Orders the LDS accesses of one wave (no other wave is involved).
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -80,13 +126,15 @@ __device__ __forceinline__ void wave_lds_sync()
 //
 // A row is read as 16-byte vectors (4 float32 or 8 bf16) when its start is
 // 16-byte aligned and V is a multiple of the vector width, else one element
-// at a time.  Values are widened to float32 in registers; bf16 widens exactly
-// (bits << 16) and narrows with round-to-nearest-even.
+// at a time.  Indices inside a row are 32-bit (rows are below 4 GiB), so a
+// load is a uniform row base plus a 32-bit per-lane offset.  A vector is held raw (Raw) in registers and widened to float32
+// where it is used; bf16 widens exactly (bits << 16) and narrows with
+// round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int DT, bool VEC>
 struct RowIO;
@@ -94,21 +142,31 @@ struct RowIO;
 template <>
 struct RowIO<kF32, true> {
     static constexpr int N = 4;
-    __device__ static void load(const void *row, int64_t v, float (&x)[N])
+    typedef u32x4 Raw;
+    __device__ static Raw load_raw(const void *row, uint32_t v)
     {
-        f32x4 r = reinterpret_cast<const f32x4 *>(row)[v];
-        x[0] = r[0]; x[1] = r[1]; x[2] = r[2]; x[3] = r[3];
+        return reinterpret_cast<const Raw *>(row)[v];
     }
-    __device__ static void store(void *row, int64_t v, const float (&g)[N])
+    __device__ static void unpack(const Raw &r, float (&x)[N])
+    {
+        // Copy each element out first: __builtin_bit_cast applied to a
+        // vector-element lvalue reads the wrong element with this compiler.
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+            const uint32_t u = r[c];
+            x[c] = __builtin_bit_cast(float, u);
+        }
+    }
+    __device__ static void store(void *row, uint32_t v, const float (&g)[N])
     {
         f32x4 r = {g[0], g[1], g[2], g[3]};
         reinterpret_cast<f32x4 *>(row)[v] = r;
     }
-    __device__ static void store_elem(void *row, int64_t j, float g)
+    __device__ static void store_elem(void *row, uint32_t j, float g)
     {
         reinterpret_cast<float *>(row)[j] = g;
     }
-    __device__ static float load_elem(const void *row, int64_t j)
+    __device__ static float load_elem(const void *row, uint32_t j)
     {
         return reinterpret_cast<const float *>(row)[j];
     }
@@ -117,27 +175,30 @@ struct RowIO<kF32, true> {
 template <>
 struct RowIO<kBF16, true> {
     static constexpr int N = 8;
-    __device__ static void load(const void *row, int64_t v, float (&x)[N])
+    typedef u32x4 Raw;
+    __device__ static Raw load_raw(const void *row, uint32_t v)
     {
-        uint4 r = reinterpret_cast<const uint4 *>(row)[v];
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+        return reinterpret_cast<const Raw *>(row)[v];
+    }
+    __device__ static void unpack(const Raw &r, float (&x)[N])
+    {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-            x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+            x[2 * i] = __builtin_bit_cast(float, r[i] << 16);
+            x[2 * i + 1] = __builtin_bit_cast(float, r[i] & 0xFFFF0000u);
         }
     }
-    __device__ static void store(void *row, int64_t v, const float (&g)[N])
+    __device__ static void store(void *row, uint32_t v, const float (&g)[N])
     {
         f32x8 f = {g[0], g[1], g[2], g[3], g[4], g[5], g[6], g[7]};
         bf16x8 b = __builtin_convertvector(f, bf16x8);
         reinterpret_cast<bf16x8 *>(row)[v] = b;
     }
-    __device__ static void store_elem(void *row, int64_t j, float g)
+    __device__ static void store_elem(void *row, uint32_t j, float g)
     {
         reinterpret_cast<__bf16 *>(row)[j] = (__bf16)g;
     }
-    __device__ static float load_elem(const void *row, int64_t j)
+    __device__ static float load_elem(const void *row, uint32_t j)
     {
         uint32_t u = reinterpret_cast<const uint16_t *>(row)[j];
         return __builtin_bit_cast(float, u << 16);
@@ -147,19 +208,21 @@ struct RowIO<kBF16, true> {
 template <>
 struct RowIO<kF32, false> {
     static constexpr int N = 1;
-    __device__ static void load(const void *row, int64_t v, float (&x)[N])
+    typedef uint32_t Raw;
+    __device__ static Raw load_raw(const void *row, uint32_t v)
     {
-        x[0] = reinterpret_cast<const float *>(row)[v];
+        return reinterpret_cast<const uint32_t *>(row)[v];
     }
-    __device__ static void store(void *row, int64_t v, const float (&g)[N])
+    __device__ static void unpack(const Raw &r, float (&x)[N]) { x[0] = __builtin_bit_cast(float, r); }
+    __device__ static void store(void *row, uint32_t v, const float (&g)[N])
     {
         reinterpret_cast<float *>(row)[v] = g[0];
     }
-    __device__ static void store_elem(void *row, int64_t j, float g)
+    __device__ static void store_elem(void *row, uint32_t j, float g)
     {
         reinterpret_cast<float *>(row)[j] = g;
     }
-    __device__ static float load_elem(const void *row, int64_t j)
+    __device__ static float load_elem(const void *row, uint32_t j)
     {
         return reinterpret_cast<const float *>(row)[j];
     }
@@ -168,25 +231,40 @@ struct RowIO<kF32, false> {
 template <>
 struct RowIO<kBF16, false> {
     static constexpr int N = 1;
-    __device__ static void load(const void *row, int64_t v, float (&x)[N])
+    typedef uint32_t Raw;
+    __device__ static Raw load_raw(const void *row, uint32_t v)
     {
-        uint32_t u = reinterpret_cast<const uint16_t *>(row)[v];
-        x[0] = __builtin_bit_cast(float, u << 16);
+        return reinterpret_cast<const uint16_t *>(row)[v];
     }
-    __device__ static void store(void *row, int64_t v, const float (&g)[N])
+    __device__ static void unpack(const Raw &r, float (&x)[N]) { x[0] = __builtin_bit_cast(float, r << 16); }
+    __device__ static void store(void *row, uint32_t v, const float (&g)[N])
     {
         reinterpret_cast<__bf16 *>(row)[v] = (__bf16)g[0];
     }
-    __device__ static void store_elem(void *row, int64_t j, float g)
+    __device__ static void store_elem(void *row, uint32_t j, float g)
     {
         reinterpret_cast<__bf16 *>(row)[j] = (__bf16)g;
     }
-    __device__ static float load_elem(const void *row, int64_t j)
+    __device__ static float load_elem(const void *row, uint32_t j)
     {
         uint32_t u = reinterpret_cast<const uint16_t *>(row)[j];
         return __builtin_bit_cast(float, u << 16);
     }
 };
+
+// A raw vector whose elements all read as -inf (padding past the row end).
+template <int DT, bool VEC>
+__device__ __forceinline__ typename RowIO<DT, VEC>::Raw neg_inf_raw()
+{
+    typename RowIO<DT, VEC>::Raw r;
+    if constexpr (VEC) {
+        const uint32_t w = DT == kF32 ? 0xFF800000u : 0xFF80FF80u;
+        r = u32x4{w, w, w, w};
+    } else {
+        r = DT == kF32 ? 0xFF800000u : 0xFF80u;
+    }
+    return r;
+}
 
 template <int DT>
 __device__ __forceinline__ size_t elt_bytes()

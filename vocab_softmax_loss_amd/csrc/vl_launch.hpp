@@ -6,6 +6,77 @@
 
 namespace vl {
 
+// The order in which a persistent grid visits the rows: the rows in the
+// loss range first (index j in [0, n_in)), then the rows outside it
+// (j in [0, n_out)).  Row r is in the range iff start <= r mod seq_len < end;
+// seq_len <= 0 means every row is.  In-range index j is row
+// (j / len_in) * seq_len + start + j % len_in; out-of-range index j is
+// position q = j % len_out of sequence j / len_out, where positions
+// [0, start) come first and then [end, seq_len).
+struct RowWalk {
+    int64_t n_in, n_out;
+    int64_t seq_len, start, len_in, len_out;
+};
+
+// Walks one of the two lists in steps of `stride` without dividing per
+// step: (seq, pos) of index j is kept and advanced by the quotient and
+// remainder of the stride, computed once.
+struct RowCursor {
+    int64_t j, seq, pos;      // current index and its (quotient, remainder)
+    int64_t len;              // list entries per sequence (len_in or len_out)
+    int64_t step_q, step_r;   // stride / len, stride % len
+
+    __host__ __device__ void init(int64_t j0, int64_t stride, int64_t l)
+    {
+        j = j0;
+        len = l > 0 ? l : 1;
+        seq = j0 / len;
+        pos = j0 % len;
+        step_q = stride / len;
+        step_r = stride % len;
+    }
+    __host__ __device__ void advance()
+    {
+        j += step_q * len + step_r;
+        seq += step_q;
+        pos += step_r;
+        if (pos >= len) {
+            pos -= len;
+            ++seq;
+        }
+    }
+    __host__ __device__ int64_t in_row(const RowWalk &w) const
+    {
+        return w.seq_len <= 0 ? j : seq * w.seq_len + w.start + pos;
+    }
+    __host__ __device__ int64_t out_row(const RowWalk &w) const
+    {
+        return seq * w.seq_len + (pos < w.start ? pos : pos + w.len_in);
+    }
+};
+
+// The two lists for `ntok` rows and the range (seq_len, start, end);
+// seq_len <= 0: every row is in the loss.
+inline RowWalk make_walk(int64_t ntok, int64_t seq_len, int64_t start, int64_t end)
+{
+    RowWalk w{};
+    if (seq_len <= 0) {
+        w.n_in = ntok;
+        return w;
+    }
+    w.seq_len = seq_len;
+    w.start = start;
+    w.len_in = end - start;
+    w.len_out = seq_len - w.len_in;
+    const int64_t full = ntok / seq_len, rem = ntok % seq_len;
+    int64_t last = (rem < end ? rem : end) - start;
+    if (last < 0)
+        last = 0;
+    w.n_in = full * w.len_in + last;
+    w.n_out = ntok - w.n_in;
+    return w;
+}
+
 // One call of the fused CE or KL row kernel.
 struct RowArgs {
     void *logits;             // [ntok][V] float32 or bf16, in: logits, out: gradient
@@ -15,7 +86,7 @@ struct RowArgs {
     float *loss;              // [ntok]
     float *lse;               // [ntok] or null
     int64_t ntok, V, k;
-    int64_t seq_len, start, end;  // loss range; seq_len <= 0: every row
+    RowWalk walk;             // loss range as a row order
     float coef;               // gradient scale
 };
 

@@ -12,25 +12,35 @@
 // the top-k).  Rows outside the loss range (start <= r mod seq_len < end)
 // are not read: their loss and lse are 0 and their gradient row is zeroed.
 //
-// One workgroup owns a row at a time (persistent grid, rows strided by the
-// grid size).  Two variants:
-//  * staged (NV > 0): the row is held in registers, NV 16-byte vectors per
-//    thread, so it is read from HBM once and written once (1R + 1W).  Each
-//    thread keeps e = exp(s - m_thread) and rescales by exp(m_thread - lse),
-//    one exp per element.
+// Schedule.  A persistent grid walks the rows in the loss first, then the
+// rows outside it, each list strided by the grid size, so every workgroup
+// gets the same share of full and write-only rows whatever the range.  One
+// workgroup owns one row at a time.  Two variants:
+//  * staged (NV > 0): the row sits in registers, NV 16-byte vectors per
+//    thread (V <= 32768 for both dtypes), so it is read from HBM once and
+//    written once (1R + 1W).  The next row's vectors are loaded into a
+//    second register buffer before the current row is reduced and stored,
+//    so HBM reads never wait for the reduction.  float32 keeps
+//    e = exp(s - m_thread) in place of s and stores e * coef *
+//    exp(m_thread - lse): one exp per element.
 //  * online (NV == 0): the row is streamed twice: pass 1 keeps a running
 //    (max, sum) per thread with one rescale per chunk, pass 2 writes the
-//    gradient (2R + 1W).
+//    gradient (2R + 1W).  One 1024-thread block per CU keeps the rows in
+//    flight small enough for the second pass to find them in the
+//    Infinity Cache.
 // (max, sum) pairs reduce across the wave with DPP and across waves through
-// LDS, one barrier per row.
+// LDS, one barrier per row (an LDS-only barrier: it does not wait for the
+// prefetched loads); the LDS slots alternate by row parity so a fast wave
+// never overwrites partials a slow wave is still reading.
 //
 // Targets.  CE: the thread that owns the label's vector subtracts coef from
 // that element before its store.  KL: the teacher ids of the row are marked
-// in an LDS bitmap of V bits; the main store skips marked elements, and the
+// in an LDS bitmap of V bits; the bulk store skips marked elements, and the
 // thread that handles id q writes coef (p_id - p_q) there itself, so every
 // element has exactly one writer (no read-modify-write of the gradient).
-// Bitmaps alternate between two LDS buffers by row parity so that clearing
-// one row's marks never races with marking the next row.
+// The two bitmaps alternate by row parity and are cleared one row late.
+// The label (scalar load), ids and probs of the next row are fetched ahead,
+// and the logits at the targets are gathered once the current row is done.
 //
 // Precondition violations are not checked on the device but never fault: a
 // label or id >= V gives a NaN loss and no target write; duplicate ids give
@@ -42,150 +52,205 @@
 
 namespace vl {
 
-__device__ __forceinline__ bool row_in_loss(int64_t r, const RowArgs &a)
-{
-    if (a.seq_len <= 0)
-        return true;
-    int64_t p = r % a.seq_len;
-    return a.start <= p && p < a.end;
-}
-
-// Vectors per thread per chunk of the online variant: 16 values in flight.
+// Vectors per thread per chunk of the online variant.
 template <int N>
 constexpr int online_unroll()
 {
-    return N >= 16 ? 1 : 16 / N;
+    return N == 1 ? 16 : 8;
 }
 
-template <int DT, bool KL, int BLOCK, int NV, bool VEC>
-__global__ __launch_bounds__(BLOCK) void row_loss_kernel(RowArgs a)
-{
+// PF (staged only): stream the next row into an LDS buffer with asynchronous
+// global-to-LDS loads while the current row, held in registers, is reduced
+// and stored.  Each lane reads back only the 16-byte slots its own loads
+// wrote, so the buffer needs no barrier, only this wave's own waits.
+// Without PF the occupancy of several blocks per CU provides the overlap.
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF>
+struct RowKernel {
     using IO = RowIO<DT, VEC>;
-    constexpr int N = IO::N;
-    constexpr int NW = BLOCK / kWave;
-    constexpr int U = online_unroll<N>();
+    using Raw = typename IO::Raw;
+    static constexpr int N = IO::N;
+    static constexpr int NW = BLOCK / kWave;
+    static constexpr int U = online_unroll<N>();
+    static constexpr int NB = NV > 0 ? NV : 1;
+    // float32 vectors hold 4 values in 4 registers, so the staged buffer can
+    // take exp(s - m) in place of s; bf16 holds 8 values in 4 registers.
+    static constexpr bool kKeepExp = (DT == kF32) && VEC && NV > 0;
 
-    __shared__ float sh_m[2][NW];
-    __shared__ float sh_s[2][NW];
-    __shared__ float sh_l[2][NW];
-    extern __shared__ uint32_t bitmaps[];  // KL: 2 x words
+    struct Tgt {
+        uint32_t label;  // CE
+        uint32_t id;     // KL: this thread's first teacher entry
+        float p;
+        float s;         // logit at the label (thread 0) or at id
+    };
 
-    const int tid = threadIdx.x;
-    const int wid = tid / kWave;
-    const int lane = lane_id();
-    const int64_t V = a.V;
-    const int64_t nvec = V / N;
-    const int words = (int)((V + 31) >> 5);
-    const float coef = a.coef;
+    const RowArgs &a;
+    float (*sh_m)[NW];
+    float (*sh_s)[NW];
+    float (*sh_l)[NW];
+    uint32_t *bitmaps;
+    Raw *pf;  // PF: BLOCK x NB vectors, slot v holds vector v of the next row
+    const int tid, wid, lane, words;
+    const uint32_t V, nvec, k;
+    const float coef;
 
-    if constexpr (KL) {
-        for (int i = tid; i < 2 * words; i += BLOCK)
-            bitmaps[i] = 0u;
-        __syncthreads();
+    __device__ RowKernel(const RowArgs &args, float (*m)[NW], float (*s)[NW], float (*l)[NW],
+                         uint32_t *bm, Raw *pfbuf)
+        : a(args), sh_m(m), sh_s(s), sh_l(l), bitmaps(bm), pf(pfbuf), tid(threadIdx.x),
+          wid(threadIdx.x / kWave), lane(lane_id()), words((int)((args.V + 31) >> 5)),
+          V((uint32_t)args.V), nvec((uint32_t)(args.V / IO::N)), k((uint32_t)args.k),
+          coef(args.coef)
+    {
     }
 
-    int par = 0;
-    for (int64_t row = blockIdx.x; row < a.ntok; row += gridDim.x) {
-        char *rowp = reinterpret_cast<char *>(a.logits) + row * V * (int64_t)elt_bytes<DT>();
+    __device__ char *rowp(int64_t row) const
+    {
+        return reinterpret_cast<char *>(a.logits) + row * (int64_t)V * (int64_t)elt_bytes<DT>();
+    }
 
-        if (!row_in_loss(row, a)) {
-            float z[N];
+    __device__ uint32_t clamp_vec(uint32_t v) const { return v < nvec ? v : nvec - 1; }
+
+    // Widen vector v; past the row end every value reads as -inf.
+    __device__ void unpack_masked(const Raw &r, uint32_t v, float (&x)[N]) const
+    {
+        IO::unpack(r, x);
+        if (v >= nvec) {
 #pragma unroll
             for (int c = 0; c < N; ++c)
-                z[c] = 0.f;
-            for (int64_t v = tid; v < nvec; v += BLOCK)
-                IO::store(rowp, v, z);
-            if (tid == 0) {
-                a.loss[row] = 0.f;
-                if (a.lse)
-                    a.lse[row] = 0.f;
-            }
-            continue;
+                x[c] = -INFINITY;
         }
+    }
 
-        uint32_t *bm = bitmaps + par * words;
-        uint32_t *bm_prev = bitmaps + (par ^ 1) * words;
+    // Loads are unconditional (index clamped into the row) and their values
+    // unused here, so the loads of a buffer issue back to back and are
+    // waited for only where the values are used.
+    __device__ void load_row(const char *p, Raw (&buf)[NB]) const
+    {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            buf[i] = IO::load_raw(p, clamp_vec(tid + (uint32_t)i * BLOCK));
+    }
 
-        // ---- targets: label, or this thread's first teacher entry
-        uint32_t label = 0;
-        float s_tgt = 0.f, p_tgt = 0.f;
-        uint32_t id_tgt = 0xFFFFFFFFu;
+    // Issued early: the label, or this thread's first id and probability.
+    __device__ void fetch_targets(int64_t row, Tgt &t) const
+    {
         if constexpr (!KL) {
-            label = a.labels[row];
-            if (tid == 0 && label < (uint32_t)V)
-                s_tgt = IO::load_elem(rowp, label);
+            // Read-only and wave-uniform: through the scalar cache, so the
+            // wait for it does not wait for the vector memory queue.
+            const __attribute__((address_space(4))) uint32_t *lab =
+                (const __attribute__((address_space(4))) uint32_t *)a.labels;
+            t.label = lab[row];
         } else {
-            const uint32_t *rid = a.ids + row * a.k;
-            for (int64_t q = tid; q < a.k; q += BLOCK) {
-                uint32_t id = rid[q];
-                if (id < (uint32_t)V)
+            t.id = 0xFFFFFFFFu;
+            t.p = 0.f;
+            if ((uint32_t)tid < k) {
+                t.id = a.ids[row * k + tid];
+                t.p = a.probs[row * k + tid];
+            }
+        }
+        t.s = 0.f;
+    }
+
+    // Once the previous row is stored: the logits at the targets and, for
+    // KL, the row's marks in bitmap `bm` (cleared by then).
+    __device__ void gather_targets(int64_t row, Tgt &t, uint32_t *bm) const
+    {
+        const char *p = rowp(row);
+        if constexpr (!KL) {
+            if (tid == 0 && t.label < V)
+                t.s = IO::load_elem(p, t.label);
+        } else {
+            for (uint32_t q = tid; q < k; q += BLOCK) {
+                const uint32_t id = q == (uint32_t)tid ? t.id : a.ids[row * k + q];
+                if (id < V) {
                     atomicOr(&bm[id >> 5], 1u << (id & 31));
-                if (q == tid) {
-                    id_tgt = id;
-                    p_tgt = a.probs[row * a.k + q];
-                    if (id < (uint32_t)V)
-                        s_tgt = IO::load_elem(rowp, id);
+                    if (q == (uint32_t)tid)
+                        t.s = IO::load_elem(p, id);
                 }
             }
         }
+    }
+
+    // The gradient of one vector, target handling included, and its store.
+    __device__ void store_vec(char *p, uint32_t v, float (&g)[N], const Tgt &t,
+                              const uint32_t *bm) const
+    {
+        if constexpr (!KL) {
+            if (t.label < V && v == t.label / N)
+                g[t.label % N] -= coef;
+            IO::store(p, v, g);
+        } else {
+            const uint32_t j0 = v * N;
+            const uint32_t bits = (bm[j0 >> 5] >> (j0 & 31)) & (uint32_t)((1ull << N) - 1);
+            if (bits == 0u) {
+                IO::store(p, v, g);
+            } else {
+#pragma unroll
+                for (int c = 0; c < N; ++c)
+                    if (!((bits >> c) & 1u))
+                        IO::store_elem(p, j0 + c, g[c]);
+            }
+        }
+    }
+
+    // One in-range row: reduce, loss, gradient.  `buf` holds the row when
+    // staged.  Afterwards the next row's targets are gathered into `tn`.
+    __device__ void process(int64_t row, Raw (&buf)[NB], Tgt &t, int par, bool has_next,
+                            int64_t nrow, Tgt &tn) const
+    {
+        char *p = rowp(row);
+        uint32_t *bm = bitmaps + par * words;
+        uint32_t *bm_other = bitmaps + (par ^ 1) * words;
 
         // ---- pass 1: thread-local (max, sum of exp)
         float m = -INFINITY, s = 0.f;
-        float x[NV > 0 ? NV : 1][N];
         if constexpr (NV > 0) {
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                int64_t v = tid + (int64_t)i * BLOCK;
-                if (v < nvec) {
-                    IO::load(rowp, v, x[i]);
-                } else {
-#pragma unroll
-                    for (int c = 0; c < N; ++c)
-                        x[i][c] = -INFINITY;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
+                float x[N];
+                unpack_masked(buf[i], tid + (uint32_t)i * BLOCK, x);
 #pragma unroll
                 for (int c = 0; c < N; ++c)
-                    m = fmaxf(m, x[i][c]);
+                    m = fmaxf(m, x[c]);
+            }
             const float ms = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
+            for (int i = 0; i < NV; ++i) {
+                float x[N];
+                unpack_masked(buf[i], tid + (uint32_t)i * BLOCK, x);
 #pragma unroll
                 for (int c = 0; c < N; ++c) {
-                    float e = __expf(x[i][c] - ms);
-                    x[i][c] = e;
+                    const float e = __expf(x[c] - ms);
                     s += e;
+                    if constexpr (kKeepExp)
+                        buf[i][c] = __builtin_bit_cast(uint32_t, e);
                 }
+            }
         } else {
-            for (int64_t v0 = tid; v0 < nvec; v0 += (int64_t)BLOCK * U) {
-                float y[U][N];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    int64_t v = v0 + (int64_t)u * BLOCK;
-                    if (v < nvec) {
-                        IO::load(rowp, v, y[u]);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < N; ++c)
-                            y[u][c] = -INFINITY;
-                    }
-                }
-                float cm = -INFINITY;
+            for (uint32_t v0 = tid; v0 < nvec; v0 += (uint32_t)BLOCK * U) {
+                Raw y[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u)
+                    y[u] = IO::load_raw(p, clamp_vec(v0 + (uint32_t)u * BLOCK));
+                float cm = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float x[N];
+                    unpack_masked(y[u], v0 + (uint32_t)u * BLOCK, x);
 #pragma unroll
                     for (int c = 0; c < N; ++c)
-                        cm = fmaxf(cm, y[u][c]);
+                        cm = fmaxf(cm, x[c]);
+                }
                 const float mn = fmaxf(m, cm);
                 if (mn != -INFINITY) {
                     float acc = s * __expf(m - mn);
 #pragma unroll
-                    for (int u = 0; u < U; ++u)
+                    for (int u = 0; u < U; ++u) {
+                        float x[N];
+                        unpack_masked(y[u], v0 + (uint32_t)u * BLOCK, x);
 #pragma unroll
                         for (int c = 0; c < N; ++c)
-                            acc += __expf(y[u][c] - mn);
+                            acc += __expf(x[c] - mn);
+                    }
                     s = acc;
                     m = mn;
                 }
@@ -202,7 +267,7 @@ __global__ __launch_bounds__(BLOCK) void row_loss_kernel(RowArgs a)
                 sh_s[par][wid] = ws;
             }
         }
-        __syncthreads();
+        block_sync_lds();
         float M = -INFINITY;
 #pragma unroll
         for (int i = 0; i < NW; ++i)
@@ -219,43 +284,41 @@ __global__ __launch_bounds__(BLOCK) void row_loss_kernel(RowArgs a)
         // ---- loss (and, for KL, the gradient at the teacher ids)
         if constexpr (!KL) {
             if (tid == 0) {
-                a.loss[row] = (label < (uint32_t)V) ? (M - s_tgt) + logS : NAN;
+                a.loss[row] = (t.label < V) ? (M - t.s) + logS : NAN;
                 if (a.lse)
                     a.lse[row] = lse;
             }
         } else {
             // The previous row's marks: every thread is past that row's stores.
             for (int i = tid; i < words; i += BLOCK)
-                bm_prev[i] = 0u;
-            const uint32_t *rid = a.ids + row * a.k;
-            const float *rp = a.probs + row * a.k;
+                bm_other[i] = 0u;
             float acc = 0.f;
-            for (int64_t q = tid; q < a.k; q += BLOCK) {
+            for (uint32_t q = tid; q < k; q += BLOCK) {
                 uint32_t id;
-                float p, sv = 0.f;
-                if (q == tid) {
-                    id = id_tgt;
-                    p = p_tgt;
-                    sv = s_tgt;
+                float pq, sv = 0.f;
+                if (q == (uint32_t)tid) {
+                    id = t.id;
+                    pq = t.p;
+                    sv = t.s;
                 } else {
-                    id = rid[q];
-                    p = rp[q];
-                    if (id < (uint32_t)V)
-                        sv = IO::load_elem(rowp, id);
+                    id = a.ids[row * k + q];
+                    pq = a.probs[row * k + q];
+                    if (id < V)
+                        sv = IO::load_elem(p, id);
                 }
-                if (id >= (uint32_t)V) {
+                if (id >= V) {
                     acc = NAN;
                     continue;
                 }
                 const float d = (sv - M) - logS;  // log p_S at the id
-                if (p > 0.f)
-                    acc += p * (__logf(p) - d);
-                IO::store_elem(rowp, id, coef * (__expf(d) - p));
+                if (pq > 0.f)
+                    acc += pq * (__logf(pq) - d);
+                IO::store_elem(p, id, coef * (__expf(d) - pq));
             }
             const float wl = wave_sum(acc);
             if (lane == 0)
                 sh_l[par][wid] = wl;
-            __syncthreads();
+            block_sync_lds();
             if (tid == 0) {
                 float tot = 0.f;
 #pragma unroll
@@ -268,64 +331,167 @@ __global__ __launch_bounds__(BLOCK) void row_loss_kernel(RowArgs a)
         }
 
         // ---- gradient store
-        auto finish = [&](int64_t v, float (&g)[N]) {
-            if constexpr (!KL) {
-                if (label < (uint32_t)V && v == (int64_t)(label / N))
-                    g[label % N] -= coef;
-                IO::store(rowp, v, g);
-            } else {
-                const int64_t j0 = v * N;
-                const uint32_t bits =
-                    (bm[j0 >> 5] >> (j0 & 31)) & (uint32_t)((1ull << N) - 1);
-                if (bits == 0u) {
-                    IO::store(rowp, v, g);
-                } else {
-#pragma unroll
-                    for (int c = 0; c < N; ++c)
-                        if (!((bits >> c) & 1u))
-                            IO::store_elem(rowp, j0 + c, g[c]);
-                }
-            }
-        };
-
         if constexpr (NV > 0) {
-            const float ms = (m == -INFINITY) ? 0.f : m;
-            const float cf = coef * __expf(ms - lse);
+            // float32 keeps e = exp(s - m_thread) in the buffer: one exp per
+            // element, p = e exp(m_thread - lse).
+            const float cf = coef * __expf(((m == -INFINITY) ? 0.f : m) - lse);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                int64_t v = tid + (int64_t)i * BLOCK;
+                const uint32_t v = tid + (uint32_t)i * BLOCK;
                 if (v < nvec) {
-                    float g[N];
+                    float x[N], g[N];
+                    IO::unpack(buf[i], x);
 #pragma unroll
                     for (int c = 0; c < N; ++c)
-                        g[c] = x[i][c] * cf;
-                    finish(v, g);
+                        g[c] = kKeepExp ? x[c] * cf : coef * __expf(x[c] - lse);
+                    store_vec(p, v, g, t, bm);
                 }
             }
         } else {
-            for (int64_t v0 = tid; v0 < nvec; v0 += (int64_t)BLOCK * U) {
-                float y[U][N];
+            for (uint32_t v0 = tid; v0 < nvec; v0 += (uint32_t)BLOCK * U) {
+                Raw y[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    y[u] = IO::load_raw(p, clamp_vec(v0 + (uint32_t)u * BLOCK));
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    int64_t v = v0 + (int64_t)u * BLOCK;
-                    if (v < nvec)
-                        IO::load(rowp, v, y[u]);
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    int64_t v = v0 + (int64_t)u * BLOCK;
+                    const uint32_t v = v0 + (uint32_t)u * BLOCK;
                     if (v < nvec) {
-                        float g[N];
+                        float x[N], g[N];
+                        IO::unpack(y[u], x);
 #pragma unroll
                         for (int c = 0; c < N; ++c)
-                            g[c] = coef * __expf(y[u][c] - lse);
-                        finish(v, g);
+                            g[c] = coef * __expf(x[c] - lse);
+                        store_vec(p, v, g, t, bm);
                     }
                 }
             }
         }
-        par ^= 1;
+
+        if (has_next)
+            gather_targets(nrow, tn, bm_other);
     }
+
+    __device__ void zero_row(int64_t row) const
+    {
+        char *p = rowp(row);
+        float z[N];
+#pragma unroll
+        for (int c = 0; c < N; ++c)
+            z[c] = 0.f;
+        for (uint32_t v = tid; v < nvec; v += BLOCK)
+            IO::store(p, v, z);
+        if (tid == 0) {
+            a.loss[row] = 0.f;
+            if (a.lse)
+                a.lse[row] = 0.f;
+        }
+    }
+
+    // PF: issue the asynchronous loads of `row` into this lane's LDS slots.
+    __device__ void prefetch_row(int64_t row) const
+    {
+        const char *p = rowp(row);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const uint32_t v = tid + (uint32_t)i * BLOCK;
+            load_to_lds16(p + (uint32_t)(clamp_vec(v) * (uint32_t)sizeof(Raw)),
+                          pf + (uint32_t)i * BLOCK + (uint32_t)wid * kWave);
+        }
+    }
+
+    // Process `row` (its targets in tc).  Staged: with PF the row is taken
+    // from this lane's LDS slots (filled during the previous step) and the
+    // next row's loads are issued into them; without PF it is loaded here.
+    // Returns whether a next row exists.
+    __device__ bool step(RowCursor &cur_pos, int64_t &row, Raw (&cur)[NB], Tgt &tc, Tgt &tn,
+                         int &par) const
+    {
+        const RowWalk &w = a.walk;
+        RowCursor nc = cur_pos;
+        nc.advance();
+        const bool has_next = nc.j < w.n_in;
+        const int64_t nrow = has_next ? nc.in_row(w) : row;
+        if constexpr (NV > 0 && PF) {
+            wait_vm_all();  // this row's loads into LDS (and all older)
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                cur[i] = pf[tid + (uint32_t)i * BLOCK];
+            wait_lds_all();  // read before the slots are refilled
+            if (has_next)
+                prefetch_row(nrow);
+        }
+        fetch_targets(nrow, tn);
+        if constexpr (NV > 0 && !PF)
+            load_row(rowp(row), cur);
+        process(row, cur, tc, par, has_next, nrow, tn);
+        par ^= 1;
+        cur_pos = nc;
+        row = nrow;
+        return has_next;
+    }
+
+    __device__ void run()
+    {
+        const RowWalk &w = a.walk;
+        if constexpr (KL) {
+            for (int i = tid; i < 2 * words; i += BLOCK)
+                bitmaps[i] = 0u;
+            block_sync_lds();
+        }
+        RowCursor c;
+        c.init(blockIdx.x, gridDim.x, w.len_in);
+        if (c.j < w.n_in) {
+            Raw buf[NB];
+            Tgt ta, tb;
+            int par = 0;
+            int64_t row = c.in_row(w);
+            fetch_targets(row, ta);
+            if constexpr (NV > 0 && PF)
+                prefetch_row(row);
+            gather_targets(row, ta, bitmaps);
+            bool more = true;
+            while (more) {
+                more = step(c, row, buf, ta, tb, par);
+                if (!more)
+                    break;
+                more = step(c, row, buf, tb, ta, par);
+            }
+        }
+        RowCursor o;
+        o.init(blockIdx.x, gridDim.x, w.len_out);
+        for (; o.j < w.n_out; o.advance())
+            zero_row(o.out_row(w));
+    }
+};
+
+// Waves per SIMD the register allocation must allow.  Staged blocks of 512
+// and 256 threads without prefetch rely on two and three resident blocks
+// per CU for their overlap; the others run one 1024-thread block per CU.
+template <int BLOCK, int NV, bool PF>
+constexpr int min_waves_per_simd()
+{
+    if (NV > 0 && !PF && BLOCK == 512)
+        return 4;
+    if (NV > 0 && !PF && BLOCK == 256)
+        return 3;
+    return 1;
+}
+
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF>
+__global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void row_loss_kernel(
+    RowArgs a)
+{
+    constexpr int NW = BLOCK / kWave;
+    __shared__ float sh_m[2][NW];
+    __shared__ float sh_s[2][NW];
+    __shared__ float sh_l[2][NW];
+    // Dynamic LDS: [PF: BLOCK x NV 16-byte slots][KL: 2 x ceil(V/32) words]
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+    using K = RowKernel<DT, KL, BLOCK, NV, VEC, PF>;
+    constexpr uint32_t pf_words = PF ? (uint32_t)BLOCK * (NV > 0 ? NV : 1) * 4 : 0;
+    K k(a, sh_m, sh_s, sh_l, dyn + pf_words, reinterpret_cast<typename K::Raw *>(dyn));
+    k.run();
 }
 
 // ------------------------------------------------------------------ launch
@@ -361,13 +527,16 @@ int cached_blocks_per_cu(const void *fn, int block, size_t lds)
     return nb;
 }
 
-template <int DT, bool KL, int BLOCK, int NV, bool VEC>
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false>
 hipError_t launch_one(const RowArgs &a, hipStream_t st)
 {
-    auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC>;
+    auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF>;
     size_t lds = 0;
-    if (KL) {
-        lds = 2 * (size_t)((a.V + 31) >> 5) * sizeof(uint32_t);
+    if (PF)
+        lds += (size_t)BLOCK * (NV > 0 ? NV : 1) * 16;
+    if (KL)
+        lds += 2 * (size_t)((a.V + 31) >> 5) * sizeof(uint32_t);
+    {
         if (lds > 65536) {
             hipError_t e = hipFuncSetAttribute((const void *)fn,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -376,17 +545,20 @@ hipError_t launch_one(const RowArgs &a, hipStream_t st)
                 return e;
         }
     }
-    const int per_cu = cached_blocks_per_cu((const void *)fn, BLOCK, lds);
+    int per_cu = cached_blocks_per_cu((const void *)fn, BLOCK, lds);
+    if (NV == 0 && per_cu > 1)
+        per_cu = 1;  // online: keep the rows in flight inside the Infinity Cache
+    const int64_t rows = a.walk.n_in > a.walk.n_out ? a.walk.n_in : a.walk.n_out;
     int64_t grid = (int64_t)per_cu * device_cus();
-    if (grid > a.ntok)
-        grid = a.ntok;
+    if (grid > rows)
+        grid = rows;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(BLOCK), lds, st, a);
     return hipGetLastError();
 }
 
 // Staged variants: BLOCK threads x NV vectors cover the row.
 template <int DT, bool KL>
-hipError_t launch_staged_or_online(const RowArgs &a, hipStream_t st, bool vec)
+hipError_t launch_dt(const RowArgs &a, hipStream_t st, bool vec)
 {
     constexpr int N = RowIO<DT, true>::N;
     if (!vec)
@@ -398,17 +570,27 @@ hipError_t launch_staged_or_online(const RowArgs &a, hipStream_t st, bool vec)
         return launch_one<DT, KL, 64, 2, true>(a, st);
     if (nvec <= 256)
         return launch_one<DT, KL, 64, 4, true>(a, st);
-    if (nvec <= 512)
-        return launch_one<DT, KL, 64, 8, true>(a, st);
-    if (nvec <= 1024)
-        return launch_one<DT, KL, 256, 4, true>(a, st);
-    if (nvec <= 2048)
-        return launch_one<DT, KL, 256, 8, true>(a, st);
-    if (nvec <= 4096)
-        return launch_one<DT, KL, 1024, 4, true>(a, st);
-    if (nvec <= 8192)
-        return launch_one<DT, KL, 1024, 8, true>(a, st);
-    return launch_one<DT, KL, 512, 0, true>(a, st);
+    if constexpr (DT == kF32) {
+        if (nvec <= 512)
+            return launch_one<DT, KL, 64, 8, true>(a, st);
+        if (nvec <= 1024)
+            return launch_one<DT, KL, 256, 4, true>(a, st);
+        if (nvec <= 2048)
+            return launch_one<DT, KL, 256, 8, true>(a, st);
+        // One 512-thread block per CU, the next row streaming into LDS.
+        if (nvec <= 4096)
+            return launch_one<DT, KL, 512, 8, true, true>(a, st);
+        if (nvec <= 8192)
+            return launch_one<DT, KL, 512, 16, true, true>(a, st);
+    } else {
+        // bf16 widens to twice its register footprint: at most 8 vectors
+        // (64 values) per thread.
+        if (nvec <= 1024)
+            return launch_one<DT, KL, 256, 4, true>(a, st);
+        if (nvec <= 4096)
+            return launch_one<DT, KL, 512, 8, true, true>(a, st);
+    }
+    return launch_one<DT, KL, 1024, 0, true>(a, st);
 }
 
 }  // namespace
@@ -419,10 +601,8 @@ hipError_t launch_rows(int dtype, bool kl, const RowArgs &a, hipStream_t st)
     const int n = 16 / (int)elt;
     const bool vec = ((uintptr_t)a.logits % 16 == 0) && (a.V % n == 0);
     if (dtype == kF32)
-        return kl ? launch_staged_or_online<kF32, true>(a, st, vec)
-                  : launch_staged_or_online<kF32, false>(a, st, vec);
-    return kl ? launch_staged_or_online<kBF16, true>(a, st, vec)
-              : launch_staged_or_online<kBF16, false>(a, st, vec);
+        return kl ? launch_dt<kF32, true>(a, st, vec) : launch_dt<kF32, false>(a, st, vec);
+    return kl ? launch_dt<kBF16, true>(a, st, vec) : launch_dt<kBF16, false>(a, st, vec);
 }
 
 }  // namespace vl

@@ -141,6 +141,7 @@ template <int DT, bool VEC, int CAP, int WPB>
 __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
 {
     using IO = RowIO<DT, VEC>;
+    using Raw = typename IO::Raw;
     constexpr int N = IO::N;
     constexpr int U = (N == 1) ? 16 : (N == 4 ? 8 : 4);
     constexpr int SUB = kWave * N;  // elements per sub-tile
@@ -168,14 +169,16 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
     bool thr_set = false;
     float thr = -INFINITY;
 
-    for (int64_t t0 = 0; t0 < nvec; t0 += (int64_t)kWave * U) {
-        float x[U][N];
+    // One tile: U sub-tiles of 64 vectors; sub-tile u of the tile at t0
+    // holds vectors t0 + 64u .. t0 + 64u + 63, lane l the vector t0 + 64u + l.
+    auto load_tile = [&](int64_t t0, Raw (&buf)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t v = t0 + (int64_t)u * kWave + lane;
-            if (v < nvec)
-                IO::load(rowp, v, x[u]);
+            buf[u] = v < nvec ? IO::load_raw(rowp, v) : neg_inf_raw<DT, VEC>();
         }
+    };
+    auto process_tile = [&](int64_t t0, const Raw (&buf)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t vbase = t0 + (int64_t)u * kWave;
@@ -183,11 +186,13 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
                 break;
             const int64_t v = vbase + lane;
             const bool valid = v < nvec;
+            float x[N];
+            IO::unpack(buf[u], x);
             if (thr_set) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int c = 0; c < N; ++c)
-                    mx = fmaxf(mx, x[u][c]);
+                    mx = fmaxf(mx, x[c]);
                 if (ballot(valid && mx > thr) == 0ull)
                     continue;
             }
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
             if (valid) {
 #pragma unroll
                 for (int c = 0; c < N; ++c)
-                    if (!thr_set || x[u][c] > thr)
+                    if (!thr_set || x[c] > thr)
                         mask |= 1u << c;
             }
             const uint32_t lc = __builtin_popcount(mask);
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
 #pragma unroll
             for (int c = 0; c < N; ++c) {
                 if ((mask >> c) & 1u) {
-                    keys[pos] = order_key(x[u][c]);
+                    keys[pos] = order_key(x[c]);
                     ids[pos] = (uint32_t)(v * N + c);
                     ++pos;
                 }
@@ -227,6 +232,25 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
             cnt += total;
             wave_lds_sync();
         }
+    };
+
+    // Double-buffered: the next tile's loads are in flight while this one
+    // is filtered.
+    constexpr int64_t TILE = (int64_t)kWave * U;
+    Raw bufA[U], bufB[U];
+    int64_t t0 = 0;
+    load_tile(0, bufA);
+    while (t0 < nvec) {
+        if (t0 + TILE < nvec)
+            load_tile(t0 + TILE, bufB);
+        process_tile(t0, bufA);
+        t0 += TILE;
+        if (t0 >= nvec)
+            break;
+        if (t0 + TILE < nvec)
+            load_tile(t0 + TILE, bufA);
+        process_tile(t0, bufB);
+        t0 += TILE;
     }
 
     // exactly k winners, in id order
