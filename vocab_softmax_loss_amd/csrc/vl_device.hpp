@@ -57,6 +57,67 @@ __device__ __forceinline__ float wave_sum(float v)
     return readlane63(v);
 }
 
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, ROW_MASK, BANK_MASK,
+                                                 BOUND_ZERO);
+}
+
+// Inclusive prefix sum over the 64 lanes.  row_shr 1..3 of the input, then
+// row_shr 4 (banks 1-3) and 8 (banks 2-3) of the running sum complete each
+// row of 16; row_bcast 15 / 31 add the totals of the rows below.
+__device__ __forceinline__ uint32_t wave_prefix_sum_u32(uint32_t x)
+{
+    uint32_t acc = x;
+    acc += dpp_u32<0x111, 0xF, 0xF, true>(0u, x);
+    acc += dpp_u32<0x112, 0xF, 0xF, true>(0u, x);
+    acc += dpp_u32<0x113, 0xF, 0xF, true>(0u, x);
+    acc += dpp_u32<0x114, 0xF, 0xE>(0u, acc);
+    acc += dpp_u32<0x118, 0xF, 0xC>(0u, acc);
+    acc += dpp_u32<0x142, 0xA, 0xF>(0u, acc);
+    acc += dpp_u32<0x143, 0xC, 0xF>(0u, acc);
+    return acc;
+}
+
+__device__ __forceinline__ uint32_t readlane63_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<0xB1>(v, v));
+    v = max(v, dpp_u32<0x4E>(v, v));
+    v = max(v, dpp_u32<0x141>(v, v));
+    v = max(v, dpp_u32<0x140>(v, v));
+    v = max(v, dpp_u32<0x142, 0xA>(v, v));
+    v = max(v, dpp_u32<0x143, 0xC>(v, v));
+    return readlane63_u32(v);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    v = min(v, dpp_u32<0xB1>(v, v));
+    v = min(v, dpp_u32<0x4E>(v, v));
+    v = min(v, dpp_u32<0x141>(v, v));
+    v = min(v, dpp_u32<0x140>(v, v));
+    v = min(v, dpp_u32<0x142, 0xA>(v, v));
+    v = min(v, dpp_u32<0x143, 0xC>(v, v));
+    return readlane63_u32(v);
+}
+
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v)
+{
+    v |= dpp_u32<0xB1>(0u, v);
+    v |= dpp_u32<0x4E>(0u, v);
+    v |= dpp_u32<0x141>(0u, v);
+    v |= dpp_u32<0x140>(0u, v);
+    v |= dpp_u32<0x142, 0xA>(0u, v);
+    v |= dpp_u32<0x143, 0xC>(0u, v);
+    return readlane63_u32(v);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }

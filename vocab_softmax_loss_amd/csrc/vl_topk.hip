@@ -9,23 +9,30 @@
 // true top-k.  This kernel is exact for every input:
 //
 // One wave owns a row and streams it once, in tiles of 64 lanes x U
-// 16-byte vectors; a tile's ids are all larger than every earlier tile's.
-// Values pass an acceptance test into a per-wave LDS candidate buffer of
-// (key, id) pairs, written in id order.  The key is the order-preserving
-// unsigned image of the float (sign-flipped, -0 folded onto +0), so key
-// order is value order.  Until the buffer first fills every value is
-// accepted; when a sub-tile might overflow it, the buffer is compacted to
-// its own top-k by an exact radix select on the keys (8-bit digits, LDS
-// histogram, 4 passes for float32, 2 for bf16 whose low key half follows
-// from the sign), keeping ties at the k-th key in buffer (= id) order.  The
-// k-th key becomes the threshold: later elements have larger ids, so only
-// values strictly above it can enter the top-k, and a quick per-vector max
-// test skips almost every sub-tile.
+// 16-byte vectors (the next tile's loads in flight while one is filtered);
+// a tile's ids are all larger than every earlier tile's.  Values pass an
+// acceptance test into a per-wave LDS candidate buffer of (key, id) pairs,
+// written in id order.  The key is the order-preserving unsigned image of
+// the float (sign-flipped, -0 folded onto +0), so key order is value order.
+// Until the buffer first fills every value is accepted; when a sub-tile
+// might overflow it, the buffer is compacted to its own top-k: an exact
+// select on the keys, then the keys above the k-th key and, of those equal
+// to it, the first ones in buffer (= id) order.  The k-th key becomes the
+// threshold: later elements have larger ids, so only values strictly above
+// it can enter the top-k, and a per-vector max test skips almost every
+// sub-tile.
 //
-// At the end the buffer is selected once more to exactly k winners, each
-// winner's output position is its rank (number of winners with a larger
-// key, plus equal keys at lower ids), and probabilities are formed from the
-// winners' values.
+// The select holds the candidates in registers and is a radix select on
+// key - min(key) over the buffer: 8-bit digits from the highest set bit of
+// the range down, counted in an LDS histogram.  Digits relative to the
+// buffer's own range spread near-equal keys over the bins (few colliding
+// LDS increments) and skip the bits every candidate shares.  Bin counts are
+// scanned across the wave with DPP.
+//
+// At the end the buffer is selected once more to exactly k winners, which
+// a register bitonic sort on (key, complemented id) puts in output order
+// (lanes exchange entries with ds_bpermute); the probabilities are formed
+// from the winners' values.
 #include <math.h>
 
 #include "vl_device.hpp"
@@ -47,94 +54,232 @@ __device__ __forceinline__ float key_value(uint32_t k)
     return __builtin_bit_cast(float, u);
 }
 
-// Exact select among keys[0..cnt): the k-th largest key kstar and how many
-// entries equal to kstar belong to the top-k (need >= 1).
-template <int DT>
-__device__ void radix_select(const uint32_t *keys, int cnt, int k, uint32_t *hist,
-                             uint32_t &kstar, int &need)
+constexpr int pow2_ceil(int x)
 {
-    const int lane = lane_id();
-    uint32_t prefix = 0u, pmask = 0u;
-    int rem = k;
-    constexpr int last = (DT == kBF16) ? 2 : 0;
-    for (int d = 3; d >= last; --d) {
-        const int shift = 8 * d;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            hist[4 * lane + j] = 0u;
-        wave_lds_sync();
-        for (int i = lane; i < cnt; i += kWave) {
-            const uint32_t key = keys[i];
-            if ((key & pmask) == prefix)
-                atomicAdd(&hist[(key >> shift) & 255u], 1u);
-        }
-        wave_lds_sync();
-        uint32_t h[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            h[j] = hist[4 * lane + j];
-        const uint32_t c = h[0] + h[1] + h[2] + h[3];
-        // inclusive suffix sum over lanes >= this lane
-        uint32_t incl = c;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t t = __shfl_down(incl, off, kWave);
-            if (lane + off < kWave)
-                incl += t;
-        }
-        uint32_t above = incl - c;  // keys in bins of higher lanes
-        int found = -1;
-        uint32_t found_above = 0u;
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-            if (found < 0 && above < (uint32_t)rem && (uint32_t)rem <= above + h[j]) {
-                found = j;
-                found_above = above;
-            }
-            above += h[j];
-        }
-        const uint64_t bl = ballot(found >= 0);
-        const int src = __builtin_ctzll(bl);
-        const int bin = __builtin_amdgcn_readlane(4 * lane + found, src);
-        const int fa = __builtin_amdgcn_readlane((int)found_above, src);
-        prefix |= (uint32_t)bin << shift;
-        pmask |= 255u << shift;
-        rem -= fa;
-    }
-    if constexpr (DT == kBF16)
-        prefix |= (prefix >> 31) ? 0u : 0xFFFFu;
-    kstar = prefix;
-    need = rem;
+    int p = 1;
+    while (p < x)
+        p <<= 1;
+    return p;
 }
 
-// Keep, in buffer order, the keys above kstar and the first `need` equal to
-// it; returns the new count (= k).
-__device__ int compact_topk(uint32_t *keys, uint32_t *ids, int cnt, uint32_t kstar, int need)
+struct Selected {
+    int cnt;        // entries kept (= k)
+    uint32_t key;   // the k-th largest key
+};
+
+// Compact the candidate buffer keys/ids[0..cnt) (cnt >= k, at most 64 E
+// entries) to its top-k, in buffer order.
+template <int E>
+__device__ __forceinline__ Selected select_compact(uint32_t *keys, uint32_t *ids, int cnt, int k,
+                                                   uint32_t *hist)
 {
     const int lane = lane_id();
+    uint32_t kr[E];
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = lane + kWave * e;
+        kr[e] = i < cnt ? keys[i] : 0u;
+        if (i < cnt) {
+            lo = min(lo, kr[e]);
+            hi = max(hi, kr[e]);
+        }
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    const uint32_t span = hi - lo;
+    // Bits below the lowest one on which rel = key - lo varies are zero in
+    // every rel (bf16 keys, for one, share their low 16 bits); no pass
+    // needs to look at them.
+    uint32_t vary = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (lane + kWave * e < cnt)
+            vary |= kr[e] - lo;
+    vary = wave_or_u32(vary);
+    const int low = vary ? __builtin_ctz(vary) : 0;
+
+    // Radix select on rel = key - lo: rel of the k-th largest key.
+    uint32_t prefix = 0u;  // the bits of that rel decided so far
+    int rem = k;           // how many of the keys matching prefix are needed
+    if (span != 0u) {
+        for (int hb = 32 - __builtin_clz(span); hb > low; hb -= 8) {
+            const int sh = hb - 8 > low ? hb - 8 : low;
+            const uint32_t dmask = (1u << (hb - sh)) - 1u;
+            const uint32_t above_mask = hb >= 32 ? 0u : ~((1u << hb) - 1u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                hist[4 * lane + j] = 0u;
+            wave_lds_sync();
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t rel = kr[e] - lo;
+                if (lane + kWave * e < cnt && (rel & above_mask) == prefix)
+                    atomicAdd(&hist[(rel >> sh) & dmask], 1u);
+            }
+            wave_lds_sync();
+            // Lane l holds bins 255-4l .. 252-4l (descending), so the
+            // exclusive prefix over lanes counts the keys in higher bins.
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                h[j] = hist[255 - 4 * lane - j];
+            const uint32_t c = h[0] + h[1] + h[2] + h[3];
+            uint32_t above = wave_prefix_sum_u32(c) - c;
+            int found = -1;
+            uint32_t found_above = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (found < 0 && above < (uint32_t)rem && (uint32_t)rem <= above + h[j]) {
+                    found = j;
+                    found_above = above;
+                }
+                above += h[j];
+            }
+            const uint64_t bl = ballot(found >= 0);
+            const int src = bl ? __builtin_ctzll(bl) : 0;
+            const uint32_t bin =
+                (uint32_t)__builtin_amdgcn_readlane(255 - 4 * lane - (found < 0 ? 0 : found), src);
+            const int fa = __builtin_amdgcn_readlane((int)found_above, src);
+            prefix |= (bin & dmask) << sh;
+            rem -= fa;
+        }
+    }
+    const uint32_t kstar = lo + prefix;
+
+    // Keep the keys above kstar and the first `rem` equal to it, in order.
+    // The buffer is rewritten in place: chunk e writes only below
+    // 64 (e + 1), and each lane reads its id before any lane writes.
     int out = 0, eq_seen = 0;
-    for (int base = 0; base < cnt; base += kWave) {
-        const int i = base + lane;
-        const bool valid = i < cnt;
-        const uint32_t key = valid ? keys[i] : 0u;
-        const uint32_t id = valid ? ids[i] : 0u;
-        const bool gt = valid && key > kstar;
-        const bool eq = valid && key == kstar;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool valid = lane + kWave * e < cnt;
+        const uint32_t id = valid ? ids[lane + kWave * e] : 0u;
+        const bool gt = valid && kr[e] > kstar;
+        const bool eq = valid && kr[e] == kstar;
         const uint64_t eqb = ballot(eq);
-        const int eq_rank = eq_seen + lanes_below(eqb);
-        const bool keep = gt || (eq && eq_rank < need);
+        const bool keep = gt || (eq && eq_seen + lanes_below(eqb) < rem);
         const uint64_t kb = ballot(keep);
-        wave_lds_sync();  // every lane has read its entry before any write
+        wave_lds_sync();
         if (keep) {
             const int pos = out + lanes_below(kb);
-            keys[pos] = key;
+            keys[pos] = kr[e];
             ids[pos] = id;
         }
         out += __builtin_popcountll(kb);
         eq_seen += __builtin_popcountll(eqb);
-        wave_lds_sync();
     }
-    return out;
+    wave_lds_sync();
+    return {out, kstar};
+}
+
+// Sort entry: the key above the bitwise complement of the id, so that
+// descending order of the pair is value descending, id ascending.  Padding
+// is 0, below every real entry (ids are below 2^32 - 1).
+__device__ __forceinline__ uint64_t sort_pair(uint32_t key, uint32_t id)
+{
+    return ((uint64_t)key << 32) | (uint32_t)~id;
+}
+
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int j)
+{
+    const int addr = (lane_id() ^ j) << 2;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange step of a bitonic sort whose partner distance
+// 64 JE is a multiple of the wave: entry i = 64 e + lane pairs with the
+// entry JE registers away in the same lane.  Blocks of kk entries whose
+// index has bit kk clear end descending, the others ascending.
+template <int JE, int EB>
+__device__ __forceinline__ void bitonic_step_regs(uint64_t (&K)[EB], int EP, int kk)
+{
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+        if ((e & JE) || (e | JE) >= EB)
+            continue;
+        if (e >= EP)
+            break;
+        const bool desc = ((e * kWave) & kk) == 0;
+        const uint64_t a = K[e], b = K[e | JE];
+        const bool sw = desc ? a < b : a > b;
+        K[e] = sw ? b : a;
+        K[e | JE] = sw ? a : b;
+    }
+}
+
+// Sort K over P = 64 EP entries (P a power of two) descending; entry i is
+// register i / 64 of lane i % 64.
+template <int EB>
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&K)[EB], int EP)
+{
+    const int lane = lane_id();
+    const int P = kWave * EP;
+    for (int kk = 2; kk <= P; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            if (j < kWave) {
+                const bool lower = (lane & j) == 0;
+#pragma unroll
+                for (int e = 0; e < EB; ++e) {
+                    if (e >= EP)
+                        break;
+                    const int i = e * kWave + lane;
+                    const bool desc = (i & kk) == 0;
+                    const uint64_t b = lane_xor_u64(K[e], j);
+                    const uint64_t a = K[e];
+                    const bool take_max = lower == desc;
+                    K[e] = take_max ? (a > b ? a : b) : (a < b ? a : b);
+                }
+            } else {
+                switch (j / kWave) {
+                case 1: bitonic_step_regs<1>(K, EP, kk); break;
+                case 2: bitonic_step_regs<2>(K, EP, kk); break;
+                case 4: bitonic_step_regs<4>(K, EP, kk); break;
+                case 8: bitonic_step_regs<8>(K, EP, kk); break;
+                case 16: bitonic_step_regs<16>(K, EP, kk); break;
+                default: bitonic_step_regs<32>(K, EP, kk); break;
+                }
+            }
+        }
+    }
+}
+
+// The k winners in keys/ids[0..k) (any order): sort them and write the ids
+// and renormalised probabilities in rank order.  EB registers per lane hold
+// up to 64 EB entries.
+template <int EB>
+__device__ __forceinline__ void write_ranked(const uint32_t *keys, const uint32_t *ids, int k, uint32_t *out_ids,
+                                             float *out_p)
+{
+    const int lane = lane_id();
+    int EP = 1;  // registers in use: 64 EP is the power of two >= k
+    while (kWave * EP < k)
+        EP <<= 1;
+    uint64_t K[EB];
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+        const int i = lane + kWave * e;
+        K[e] = i < k ? sort_pair(keys[i], ids[i]) : 0ull;
+    }
+    bitonic_sort_desc<EB>(K, EP);
+
+    const float v0 = key_value((uint32_t)(__builtin_amdgcn_readlane((int)(uint32_t)(K[0] >> 32), 0)));
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < EB; ++e)
+        if (lane + kWave * e < k)
+            z += __expf(key_value((uint32_t)(K[e] >> 32)) - v0);
+    const float Z = wave_sum(z);
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+        const int i = lane + kWave * e;
+        if (i < k) {
+            out_ids[i] = ~(uint32_t)K[e];
+            out_p[i] = __expf(key_value((uint32_t)(K[e] >> 32)) - v0) / Z;
+        }
+    }
 }
 
 template <int DT, bool VEC, int CAP, int WPB>
@@ -143,8 +288,12 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
     using IO = RowIO<DT, VEC>;
     using Raw = typename IO::Raw;
     constexpr int N = IO::N;
-    constexpr int U = (N == 1) ? 16 : (N == 4 ? 8 : 4);
+    constexpr int U = (N == 1) ? 16 : 4;
     constexpr int SUB = kWave * N;  // elements per sub-tile
+    constexpr int E = CAP / kWave;
+    // k <= min(CAP - SUB, kMaxTopk); the sort pads k to a power of two.
+    constexpr int kMaxK = (CAP - SUB) < kMaxTopk ? (CAP - SUB) : (int)kMaxTopk;
+    constexpr int kSortRegs = pow2_ceil(kMaxK) / kWave > 0 ? pow2_ceil(kMaxK) / kWave : 1;
 
     __shared__ uint32_t s_key[WPB][CAP];
     __shared__ uint32_t s_id[WPB][CAP];
@@ -160,10 +309,9 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
     uint32_t *ids = s_id[w];
     uint32_t *hist = s_hist[w];
     const int k = (int)a.k;
-    const int64_t V = a.V;
-    const int64_t nvec = V / N;
+    const uint32_t nvec = (uint32_t)(a.V / N);
     const char *rowp =
-        reinterpret_cast<const char *>(a.logits) + row * V * (int64_t)elt_bytes<DT>();
+        reinterpret_cast<const char *>(a.logits) + row * a.V * (int64_t)elt_bytes<DT>();
 
     int cnt = 0;
     bool thr_set = false;
@@ -171,20 +319,21 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
 
     // One tile: U sub-tiles of 64 vectors; sub-tile u of the tile at t0
     // holds vectors t0 + 64u .. t0 + 64u + 63, lane l the vector t0 + 64u + l.
-    auto load_tile = [&](int64_t t0, Raw (&buf)[U]) {
+    // Loads are unconditional (index clamped into the row).
+    auto load_tile = [&](uint32_t t0, Raw (&buf)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t v = t0 + (int64_t)u * kWave + lane;
-            buf[u] = v < nvec ? IO::load_raw(rowp, v) : neg_inf_raw<DT, VEC>();
+            const uint32_t v = t0 + (uint32_t)u * kWave + lane;
+            buf[u] = IO::load_raw(rowp, v < nvec ? v : nvec - 1);
         }
     };
-    auto process_tile = [&](int64_t t0, const Raw (&buf)[U]) {
+    auto process_tile = [&](uint32_t t0, const Raw (&buf)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t vbase = t0 + (int64_t)u * kWave;
+            const uint32_t vbase = t0 + (uint32_t)u * kWave;
             if (vbase >= nvec)
                 break;
-            const int64_t v = vbase + lane;
+            const uint32_t v = vbase + lane;
             const bool valid = v < nvec;
             float x[N];
             IO::unpack(buf[u], x);
@@ -197,12 +346,10 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
                     continue;
             }
             if (cnt + SUB > CAP) {
-                uint32_t kstar;
-                int need;
-                radix_select<DT>(keys, cnt, k, hist, kstar, need);
-                cnt = compact_topk(keys, ids, cnt, kstar, need);
+                const Selected sel = select_compact<E>(keys, ids, cnt, k, hist);
+                cnt = sel.cnt;
+                thr = key_value(sel.key);
                 thr_set = true;
-                thr = key_value(kstar);
             }
             uint32_t mask = 0u;
             if (valid) {
@@ -211,83 +358,68 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
                     if (!thr_set || x[c] > thr)
                         mask |= 1u << c;
             }
-            const uint32_t lc = __builtin_popcount(mask);
-            // exclusive prefix of lc over lanes, bit-sliced (lc <= 8)
-            int prefix = 0, total = 0;
+            if (ballot((mask & (mask - 1u)) != 0u) == 0ull) {
+                // Common case: at most one candidate per lane; lane order
+                // is id order.
+                const uint64_t has = ballot(mask != 0u);
+                if (mask) {
+                    const int c = __builtin_ctz(mask);
+                    float xc = x[0];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint64_t bb = ballot((lc >> b) & 1u);
-                prefix += lanes_below(bb) << b;
-                total += __builtin_popcountll(bb) << b;
-            }
-            int pos = cnt + prefix;
-#pragma unroll
-            for (int c = 0; c < N; ++c) {
-                if ((mask >> c) & 1u) {
-                    keys[pos] = order_key(x[c]);
-                    ids[pos] = (uint32_t)(v * N + c);
-                    ++pos;
+                    for (int cc = 1; cc < N; ++cc)
+                        xc = c == cc ? x[cc] : xc;
+                    const int pos = cnt + lanes_below(has);
+                    keys[pos] = order_key(xc);
+                    ids[pos] = v * N + c;
                 }
+                cnt += __builtin_popcountll(has);
+            } else {
+                const uint32_t lc = __builtin_popcount(mask);
+                // exclusive prefix of lc over lanes, bit-sliced (lc <= 8)
+                int prefix = 0, total = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint64_t bb = ballot((lc >> b) & 1u);
+                    prefix += lanes_below(bb) << b;
+                    total += __builtin_popcountll(bb) << b;
+                }
+                int pos = cnt + prefix;
+#pragma unroll
+                for (int c = 0; c < N; ++c) {
+                    if ((mask >> c) & 1u) {
+                        keys[pos] = order_key(x[c]);
+                        ids[pos] = v * N + c;
+                        ++pos;
+                    }
+                }
+                cnt += total;
             }
-            cnt += total;
             wave_lds_sync();
         }
     };
 
-    // Double-buffered: the next tile's loads are in flight while this one
-    // is filtered.
-    constexpr int64_t TILE = (int64_t)kWave * U;
+    // The next tile is always loaded (past the row end the clamped index
+    // re-reads its last vector), so every iteration issues the same loads
+    // and the waits derived for the current tile never cover the next one.
+    constexpr uint32_t TILE = (uint32_t)kWave * U;
     Raw bufA[U], bufB[U];
-    int64_t t0 = 0;
+    uint32_t t0 = 0;
     load_tile(0, bufA);
     while (t0 < nvec) {
-        if (t0 + TILE < nvec)
-            load_tile(t0 + TILE, bufB);
+        load_tile(t0 + TILE, bufB);
         process_tile(t0, bufA);
         t0 += TILE;
         if (t0 >= nvec)
             break;
-        if (t0 + TILE < nvec)
-            load_tile(t0 + TILE, bufA);
+        load_tile(t0 + TILE, bufA);
         process_tile(t0, bufB);
         t0 += TILE;
     }
 
-    // exactly k winners, in id order
-    {
-        uint32_t kstar;
-        int need;
-        wave_lds_sync();
-        radix_select<DT>(keys, cnt, k, hist, kstar, need);
-        cnt = compact_topk(keys, ids, cnt, kstar, need);
-    }
-
-    // renormalised probabilities over the k winners
-    float vmax = -INFINITY;
-    for (int i = lane; i < k; i += kWave)
-        vmax = fmaxf(vmax, key_value(keys[i]));
-    const float v0 = wave_max(vmax);
-    float z = 0.f;
-    for (int i = lane; i < k; i += kWave)
-        z += __expf(key_value(keys[i]) - v0);
-    const float Z = wave_sum(z);
-
-    uint32_t *out_ids = a.ids + row * a.k;
-    float *out_p = a.probs + row * a.k;
-    for (int i0 = 0; i0 < k; i0 += kWave) {
-        const int i = i0 + lane;
-        const bool valid = i < k;
-        const uint32_t ki = valid ? keys[i] : 0u;
-        int rank = 0;
-        for (int j = 0; j < k; ++j) {
-            const uint32_t kj = keys[j];
-            rank += (kj > ki) || (kj == ki && j < i);
-        }
-        if (valid) {
-            out_ids[rank] = ids[i];
-            out_p[rank] = __expf(key_value(ki) - v0) / Z;
-        }
-    }
+    // exactly k winners, in id order, then written at their ranks
+    wave_lds_sync();
+    select_compact<E>(keys, ids, cnt, k, hist);  // leaves exactly k entries
+    write_ranked<kSortRegs>(keys, ids, k, a.ids + row * a.k, a.probs + row * a.k);
 }
 
 namespace {
