@@ -18,10 +18,21 @@ Prints one JSON line.  `value` is logits rows per second of the whole step;
 the launch stream around every launch of the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-                    [--workload step|ce_lm|topk_zipf|kl_large|kl_bf16]
+                    [--workload step|ce_lm|topk_zipf|kl_large|kl_bf16|copy_calib]
+    python bench.py --pmc-summary <counter_collection.csv> ...
 
-The other workloads time one configuration each at its full size (for the
-per-kernel rooflines in the design doc); the default line is the step above.
+The other workloads time one configuration each at its full size, for
+per-kernel rooflines; the default line is the step above.
+`copy_calib` times a plain 1 GiB device-to-device copy, the known-size
+kernel that scales the HBM byte counters.
+
+`roofline.traffic` is the dominant kernel's HBM bytes per launch as the
+FETCH_SIZE and WRITE_SIZE counters read it (two separate rocprofv3 --pmc
+runs of this script), each scaled by bytes / counter of the 1 GiB copy.
+The figures live in profiles/hbm_traffic_step_4096x32000_f32.md together
+with a SHA-256 of the kernel sources they were taken with; when the sources
+differ from that hash, traffic is null.  `--pmc-summary` averages a
+rocprofv3 counter CSV per kernel and counter, the numbers that file holds.
 """
 from __future__ import annotations
 
@@ -35,6 +46,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_step_4096x32000_f32.md")
+KERNEL_SOURCES = ("vl_device.hpp", "vl_launch.hpp", "vl_rows.hip", "vl_topk.hip", "vl_acc.hip")
+COPY_CALIB_BYTES = 1 << 30
 
 NTOK, V, K_TOPK, HS = 4096, 32000, 64, 1024
 NSEQ, SEQ_LEN, PROMPT = 8, 512, 128
@@ -42,7 +56,7 @@ NSEQ, SEQ_LEN, PROMPT = 8, 512, 128
 
 def algorithmic_bytes():
     """Bytes each kernel must move per launch (each input read once, each
-    output written once; see the design doc for the per-row figures)."""
+    output written once)."""
     row = V * 4
     n_in = NSEQ * (SEQ_LEN - PROMPT)
     return {
@@ -151,9 +165,58 @@ def other_workload(name, dev):
                   "acc": 3 * ntok * hs * 4}
         cfg = {"workload": gi.KL_BF16.name, "ntok": ntok, "V": V, "k": k, "dtype": "bf16",
                "bytes_model": "KL 2R+1W"}
+    elif name == "copy_calib":
+        n = COPY_CALIB_BYTES // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        calls = [("copy", lambda: dst.copy_(src))]
+        nbytes = {"copy": 2 * COPY_CALIB_BYTES}
+        ntok = 1
+        cfg = {"workload": "plain device copy of 1 GiB float32 (counter calibration)",
+               "bytes": COPY_CALIB_BYTES, "dtype": "f32"}
     else:
         raise SystemExit(f"unknown workload {name}")
     return calls, nbytes, ntok, cfg
+
+
+def kernel_sources_sha256():
+    """SHA-256 over the HIP kernel sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "vocab_softmax_loss_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` in the step, from the counter file,
+    or None when the file is missing, lacks the kernel or was taken with
+    other kernel sources."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^kernel_sources_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not m or m.group(1) != kernel_sources_sha256():
+        return None
+    m = re.search(rf"^traffic_bytes\.{kernel}: (\d+)$", text, re.M)
+    return int(m.group(1)) if m else None
+
+
+def pmc_summary(paths):
+    """Per kernel and counter: dispatches and mean value, from rocprofv3
+    counter_collection CSVs."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for p in paths:
+        with open(p) as fh:
+            for r in csv.DictReader(fh):
+                acc[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    for (kern, ctr), v in sorted(acc.items()):
+        print(f"{ctr}\t{len(v)}\t{sum(v) / len(v):.1f}\t{kern}")
 
 
 def time_calls(calls, steps, warmup):
@@ -198,10 +261,14 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=NTOK)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default="step")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="CSV")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs on a single MI355X "
-              "(rows shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+              "(token rows shard across GPUs with no exchange between them).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -244,7 +311,7 @@ def main():
     dom = max(per_kernel_ms, key=per_kernel_ms.get)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB/s"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
-                "traffic": None}
+                "traffic": measured_traffic(dom)}
 
     cpu = None
     if not args.no_cpu:

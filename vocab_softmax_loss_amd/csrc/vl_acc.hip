@@ -23,7 +23,7 @@ __global__ __launch_bounds__(kAccBlock) void slice_acc_vec_kernel(f32x4 *dst, co
         a[1] += b[1];
         a[2] += b[2];
         a[3] += b[3];
-        dst[i] = a;
+        __builtin_nontemporal_store(a, dst + i);  // written once: keep it out of the caches
     }
 }
 

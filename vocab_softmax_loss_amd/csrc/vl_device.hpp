@@ -218,10 +218,19 @@ struct RowIO<kF32, true> {
             x[c] = __builtin_bit_cast(float, u);
         }
     }
+    // A read that nothing re-reads soon (nt): it does not displace what the
+    // caches hold, so it does not force out their dirty lines either.
+    __device__ static Raw load_stream(const void *row, uint32_t v)
+    {
+        return __builtin_nontemporal_load(reinterpret_cast<const Raw *>(row) + v);
+    }
+    // Gradient rows are written once and exceed every cache: nt stores keep
+    // them from sitting dirty in the last-level cache, whose write-back
+    // would otherwise fall inside the next kernel.
     __device__ static void store(void *row, uint32_t v, const float (&g)[N])
     {
         f32x4 r = {g[0], g[1], g[2], g[3]};
-        reinterpret_cast<f32x4 *>(row)[v] = r;
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4 *>(row) + v);
     }
     __device__ static void store_elem(void *row, uint32_t j, float g)
     {
@@ -240,6 +249,10 @@ struct RowIO<kBF16, true> {
     __device__ static Raw load_raw(const void *row, uint32_t v)
     {
         return reinterpret_cast<const Raw *>(row)[v];
+    }
+    __device__ static Raw load_stream(const void *row, uint32_t v)
+    {
+        return __builtin_nontemporal_load(reinterpret_cast<const Raw *>(row) + v);
     }
     __device__ static void unpack(const Raw &r, float (&x)[N])
     {
@@ -274,6 +287,10 @@ struct RowIO<kF32, false> {
     {
         return reinterpret_cast<const uint32_t *>(row)[v];
     }
+    __device__ static Raw load_stream(const void *row, uint32_t v)
+    {
+        return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(row) + v);
+    }
     __device__ static void unpack(const Raw &r, float (&x)[N]) { x[0] = __builtin_bit_cast(float, r); }
     __device__ static void store(void *row, uint32_t v, const float (&g)[N])
     {
@@ -296,6 +313,10 @@ struct RowIO<kBF16, false> {
     __device__ static Raw load_raw(const void *row, uint32_t v)
     {
         return reinterpret_cast<const uint16_t *>(row)[v];
+    }
+    __device__ static Raw load_stream(const void *row, uint32_t v)
+    {
+        return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(row) + v);
     }
     __device__ static void unpack(const Raw &r, float (&x)[N]) { x[0] = __builtin_bit_cast(float, r << 16); }
     __device__ static void store(void *row, uint32_t v, const float (&g)[N])

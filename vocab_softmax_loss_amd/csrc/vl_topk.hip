@@ -319,12 +319,13 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
 
     // One tile: U sub-tiles of 64 vectors; sub-tile u of the tile at t0
     // holds vectors t0 + 64u .. t0 + 64u + 63, lane l the vector t0 + 64u + l.
-    // Loads are unconditional (index clamped into the row).
+    // Loads are unconditional (index clamped into the row) and non-temporal:
+    // the row is read once.
     auto load_tile = [&](uint32_t t0, Raw (&buf)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t v = t0 + (uint32_t)u * kWave + lane;
-            buf[u] = IO::load_raw(rowp, v < nvec ? v : nvec - 1);
+            buf[u] = IO::load_stream(rowp, v < nvec ? v : nvec - 1);
         }
     };
     auto process_tile = [&](uint32_t t0, const Raw (&buf)[U]) {
