@@ -187,9 +187,10 @@ __device__ __forceinline__ void wave_lds_sync()
 //
 // A row is read as 16-byte vectors (4 float32 or 8 bf16) when its start is
 // 16-byte aligned and V is a multiple of the vector width, else one element
-// at a time.  Indices inside a row are 32-bit (rows are below 4 GiB), so a
-// load is a uniform row base plus a 32-bit per-lane offset.  A vector is held raw (Raw) in registers and widened to float32
-// where it is used; bf16 widens exactly (bits << 16) and narrows with
+// at a time.  Vector and element indices inside a row are 32-bit (V is
+// below 2^31); addresses are the row base plus the index scaled in 64 bits.
+// A vector is held raw (Raw) in registers and widened to float32 where it
+// is used; bf16 widens exactly (bits << 16) and narrows with
 // round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

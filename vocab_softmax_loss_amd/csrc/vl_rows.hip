@@ -395,7 +395,7 @@ struct RowKernel {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const uint32_t v = tid + (uint32_t)i * BLOCK;
-            load_to_lds16(p + (uint32_t)(clamp_vec(v) * (uint32_t)sizeof(Raw)),
+            load_to_lds16(p + (size_t)clamp_vec(v) * sizeof(Raw),
                           pf + (uint32_t)i * BLOCK + (uint32_t)wid * kWave);
         }
     }
