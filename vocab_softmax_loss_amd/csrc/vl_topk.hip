@@ -63,15 +63,21 @@ constexpr int pow2_ceil(int x)
 }
 
 struct Selected {
-    int cnt;        // entries kept (= k)
-    uint32_t key;   // the k-th largest key
+    int cnt;        // entries kept
+    uint32_t key;   // exact: the k-th largest key; else the smallest key kept
 };
 
 // Compact the candidate buffer keys/ids[0..cnt) (cnt >= k, at most 64 E
-// entries) to its top-k, in buffer order.
+// entries), in buffer order.
+//   limit == 0: to its top-k exactly (the k-th largest key, and of the keys
+//               equal to it only the first ones).
+//   limit > 0:  to every key >= some bound that at least k keys reach; the
+//               radix passes stop as soon as that keeps at most `limit`
+//               entries.  Whatever it keeps holds the top-k, and a later
+//               element (larger id) not above the bound cannot enter it.
 template <int E>
 __device__ __forceinline__ Selected select_compact(uint32_t *keys, uint32_t *ids, int cnt, int k,
-                                                   uint32_t *hist)
+                                                   uint32_t *hist, int limit = 0)
 {
     const int lane = lane_id();
     uint32_t kr[E];
@@ -102,6 +108,7 @@ __device__ __forceinline__ Selected select_compact(uint32_t *keys, uint32_t *ids
     // Radix select on rel = key - lo: rel of the k-th largest key.
     uint32_t prefix = 0u;  // the bits of that rel decided so far
     int rem = k;           // how many of the keys matching prefix are needed
+    bool keep_ge = false;  // stopped early: keep every rel >= prefix
     if (span != 0u) {
         for (int hb = 32 - __builtin_clz(span); hb > low; hb -= 8) {
             const int sh = hb - 8 > low ? hb - 8 : low;
@@ -138,10 +145,18 @@ __device__ __forceinline__ Selected select_compact(uint32_t *keys, uint32_t *ids
             }
             const uint64_t bl = ballot(found >= 0);
             const int src = bl ? __builtin_ctzll(bl) : 0;
-            const uint32_t bin =
-                (uint32_t)__builtin_amdgcn_readlane(255 - 4 * lane - (found < 0 ? 0 : found), src);
+            const int fj = found < 0 ? 0 : found;
+            const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(255 - 4 * lane - fj, src);
             const int fa = __builtin_amdgcn_readlane((int)found_above, src);
+            const uint32_t hb_cnt = fj == 0 ? h[0] : fj == 1 ? h[1] : fj == 2 ? h[2] : h[3];
+            const int in_bin = __builtin_amdgcn_readlane((int)hb_cnt, src);
             prefix |= (bin & dmask) << sh;
+            // keys >= the bin's lower edge: those above the decided digits,
+            // those in higher bins of this pass, and the bin itself
+            if (limit > 0 && (k - rem) + fa + in_bin <= limit) {
+                keep_ge = true;
+                break;
+            }
             rem -= fa;
         }
     }
@@ -158,7 +173,7 @@ __device__ __forceinline__ Selected select_compact(uint32_t *keys, uint32_t *ids
         const bool gt = valid && kr[e] > kstar;
         const bool eq = valid && kr[e] == kstar;
         const uint64_t eqb = ballot(eq);
-        const bool keep = gt || (eq && eq_seen + lanes_below(eqb) < rem);
+        const bool keep = gt || (eq && (keep_ge || eq_seen + lanes_below(eqb) < rem));
         const uint64_t kb = ballot(keep);
         wave_lds_sync();
         if (keep) {
@@ -282,8 +297,12 @@ __device__ __forceinline__ void write_ranked(const uint32_t *keys, const uint32_
     }
 }
 
+// Up to CAP 1024 the register budget is held to four waves per SIMD (128
+// VGPRs): the 1024-entry bf16 variant would otherwise take 138 and run three
+// waves per SIMD, 11% slower at 16384 x 151936 despite a few spilled
+// registers in its compaction.
 template <int DT, bool VEC, int CAP, int WPB>
-__global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
+__global__ __launch_bounds__(WPB * kWave, (CAP <= 1024 ? 4 : 1)) void topk_kernel(TopkArgs a)
 {
     using IO = RowIO<DT, VEC>;
     using Raw = typename IO::Raw;
@@ -309,6 +328,9 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
     uint32_t *ids = s_id[w];
     uint32_t *hist = s_hist[w];
     const int k = (int)a.k;
+    // Mid-row compactions may stop at a bound that keeps up to this many
+    // entries: a quarter of the way from k to the next compaction's trigger.
+    const int kSelLimit = k + (CAP - SUB - k) / 4;
     const uint32_t nvec = (uint32_t)(a.V / N);
     const char *rowp =
         reinterpret_cast<const char *>(a.logits) + row * a.V * (int64_t)elt_bytes<DT>();
@@ -347,7 +369,7 @@ __global__ __launch_bounds__(WPB * kWave) void topk_kernel(TopkArgs a)
                     continue;
             }
             if (cnt + SUB > CAP) {
-                const Selected sel = select_compact<E>(keys, ids, cnt, k, hist);
+                const Selected sel = select_compact<E>(keys, ids, cnt, k, hist, kSelLimit);
                 cnt = sel.cnt;
                 thr = key_value(sel.key);
                 thr_set = true;
