@@ -162,6 +162,32 @@ def test_ce_lm_small(vl):
     assert_ce(vl, c["logits"], c["labels"], c["rng"], c["scale"])
 
 
+# Several rows per workgroup: the persistent grid has at most a few blocks
+# per CU, so 600+ rows give every block a sequence of rows, which exercises
+# the next-row pipelines (LDS prefetch, register refill) and the row-parity
+# LDS buffers.  V picks the variant: 32000 float32 and 30000 bf16 are staged
+# with an LDS prefetch, 40008 float32 is online, 40008 bf16 refills
+# registers, 8000 bf16 runs two blocks per CU.
+MULTIROW = [("f32", 32000), ("bf16", 30000), ("f32", 40008), ("bf16", 40008), ("bf16", 8000)]
+
+
+@pytest.mark.parametrize("dtype,V", MULTIROW)
+def test_ce_multirow(vl, dtype, V):
+    ntok = 640
+    x = gi.normal_logits(ntok, V, 3.0, 600 + V, DEV, TDT[dtype])
+    lab = gi.uniform_labels(ntok, V, 700 + V, DEV)
+    assert_ce(vl, x, lab, (160, 40, 150), 1.0 / 440)
+
+
+@pytest.mark.parametrize("dtype,V", MULTIROW)
+def test_kl_multirow(vl, dtype, V):
+    ntok, k = 640, 96
+    x = gi.normal_logits(ntok, V, 2.0, 800 + V, DEV, TDT[dtype])
+    ids = gi.distinct_ids(ntok, V, k, 900 + V, DEV)
+    probs = gi.softmax_probs(ntok, k, 1.5, 1000 + V, DEV)
+    assert_kl(vl, x, ids, probs, None, 1024.0 / ntok)
+
+
 # ------------------------------------------------------------ KL
 
 KL_VK = [(1, 1), (8, 3), (512, 16), (1001, 64), (2049, 5), (8192, 128), (32000, 64),

@@ -17,10 +17,13 @@
 // gets the same share of full and write-only rows whatever the range.  One
 // workgroup owns one row at a time.  Two variants:
 //  * staged (NV > 0): the row sits in registers, NV 16-byte vectors per
-//    thread (V <= 32768 for both dtypes), so it is read from HBM once and
-//    written once (1R + 1W).  The next row's vectors are loaded into a
-//    second register buffer before the current row is reduced and stored,
-//    so HBM reads never wait for the reduction.  float32 keeps
+//    thread (V <= 32768 float32, V <= 155648 bf16), so it is read from HBM
+//    once and written once (1R + 1W).  How the next row's reads overlap the
+//    current row depends on the shape: several blocks per CU (small
+//    blocks); an asynchronous copy of the next row into LDS (PF, one
+//    512-thread block per CU); or, for rows that fill a 1024-thread
+//    block's registers, each register refilled with the next row's vector
+//    right after its gradient is stored (RL).  float32 keeps
 //    e = exp(s - m_thread) in place of s and stores e * coef *
 //    exp(m_thread - lse): one exp per element.
 //  * online (NV == 0): the row is streamed twice: pass 1 keeps a running
@@ -64,7 +67,7 @@ constexpr int online_unroll()
 // and stored.  Each lane reads back only the 16-byte slots its own loads
 // wrote, so the buffer needs no barrier, only this wave's own waits.
 // Without PF the occupancy of several blocks per CU provides the overlap.
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF>
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL>
 struct RowKernel {
     using IO = RowIO<DT, VEC>;
     using Raw = typename IO::Raw;
@@ -109,6 +112,45 @@ struct RowKernel {
 
     __device__ uint32_t clamp_vec(uint32_t v) const { return v < nvec ? v : nvec - 1; }
 
+    // Staged rows (NV > 0, always 16-byte vectors) are far below 4 GiB, so
+    // vector v is at a 32-bit byte offset from the row base: one offset
+    // register per load, with the base in scalar registers.
+    __device__ static Raw load_small(const char *p, uint32_t v)
+    {
+        return *reinterpret_cast<const Raw *>(p + v * (uint32_t)sizeof(Raw));
+    }
+
+    // The thread index as a value the compiler cannot see through: per-row
+    // index arithmetic is then redone per row (a few adds) instead of being
+    // hoisted out of the row loop and kept live, one register pair per
+    // vector, beside the row itself.
+    __device__ uint32_t fresh_tid() const
+    {
+        uint32_t t = (uint32_t)tid;
+        __asm__ __volatile__("" : "+v"(t));
+        return t;
+    }
+
+    // Hide the buffer's contents from the compiler until `dep` is known, so
+    // that a pass widens the raw vectors again after the previous pass's
+    // result instead of keeping that pass's widened values alive (8
+    // registers per bf16 vector instead of 4).
+    __device__ static void opaque(Raw (&buf)[NB], float dep)
+    {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            __asm__ __volatile__("" : "+v"(buf[i]) : "v"(dep));
+    }
+
+    // With a whole long row per thread (RL), the scheduler may not start the
+    // next vector of a pass before this one is consumed: interleaving them
+    // widens many vectors at once and spills.
+    __device__ static void vector_fence()
+    {
+        if constexpr (RL)
+            __builtin_amdgcn_sched_barrier(0);
+    }
+
     // Widen vector v; past the row end every value reads as -inf.
     __device__ void unpack_masked(const Raw &r, uint32_t v, float (&x)[N]) const
     {
@@ -127,7 +169,7 @@ struct RowKernel {
     {
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            buf[i] = IO::load_raw(p, clamp_vec(tid + (uint32_t)i * BLOCK));
+            buf[i] = load_small(p, clamp_vec(tid + (uint32_t)i * BLOCK));
     }
 
     // Issued early: the label, or this thread's first id and probability.
@@ -174,56 +216,70 @@ struct RowKernel {
     __device__ void store_vec(char *p, uint32_t v, float (&g)[N], const Tgt &t,
                               const uint32_t *bm) const
     {
+        // Staged rows: vector v at a 32-bit byte offset (see load_small).
+        char *q = NV > 0 ? p + v * (uint32_t)(N * elt_bytes<DT>()) : p;
+        const uint32_t vi = NV > 0 ? 0u : v;  // vector index from q
         if constexpr (!KL) {
             if (t.label < V && v == t.label / N)
                 g[t.label % N] -= coef;
-            IO::store(p, v, g);
+            IO::store(q, vi, g);
         } else {
             const uint32_t j0 = v * N;
             const uint32_t bits = (bm[j0 >> 5] >> (j0 & 31)) & (uint32_t)((1ull << N) - 1);
             if (bits == 0u) {
-                IO::store(p, v, g);
+                IO::store(q, vi, g);
             } else {
 #pragma unroll
                 for (int c = 0; c < N; ++c)
                     if (!((bits >> c) & 1u))
-                        IO::store_elem(p, j0 + c, g[c]);
+                        IO::store_elem(q, vi * N + c, g[c]);
             }
         }
     }
 
     // One in-range row: reduce, loss, gradient.  `buf` holds the row when
-    // staged.  Afterwards the next row's targets are gathered into `tn`.
+    // staged; with RL each register is refilled with the next row's vector
+    // as soon as its own gradient is stored.  Afterwards the next row's
+    // targets are gathered into `tn`.
     __device__ void process(int64_t row, Raw (&buf)[NB], Tgt &t, int par, bool has_next,
                             int64_t nrow, Tgt &tn) const
     {
         char *p = rowp(row);
         uint32_t *bm = bitmaps + par * words;
         uint32_t *bm_other = bitmaps + (par ^ 1) * words;
+        const uint32_t t0 = fresh_tid();
 
         // ---- pass 1: thread-local (max, sum of exp)
         float m = -INFINITY, s = 0.f;
         if constexpr (NV > 0) {
+            // Vectors past the row end hold a copy of its last vector (the
+            // loads are clamped): harmless to the max, left out of the sum.
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 float x[N];
-                unpack_masked(buf[i], tid + (uint32_t)i * BLOCK, x);
+                IO::unpack(buf[i], x);
 #pragma unroll
                 for (int c = 0; c < N; ++c)
                     m = fmaxf(m, x[c]);
+                vector_fence();
             }
             const float ms = (m == -INFINITY) ? 0.f : m;
+            if constexpr (!kKeepExp)
+                opaque(buf, ms);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 float x[N];
-                unpack_masked(buf[i], tid + (uint32_t)i * BLOCK, x);
+                IO::unpack(buf[i], x);
+                float es = 0.f;
 #pragma unroll
                 for (int c = 0; c < N; ++c) {
                     const float e = __expf(x[c] - ms);
-                    s += e;
+                    es += e;
                     if constexpr (kKeepExp)
                         buf[i][c] = __builtin_bit_cast(uint32_t, e);
                 }
+                s += (t0 + (uint32_t)i * BLOCK < nvec) ? es : 0.f;
+                vector_fence();
             }
         } else {
             for (uint32_t v0 = tid; v0 < nvec; v0 += (uint32_t)BLOCK * U) {
@@ -335,9 +391,13 @@ struct RowKernel {
             // float32 keeps e = exp(s - m_thread) in the buffer: one exp per
             // element, p = e exp(m_thread - lse).
             const float cf = coef * __expf(((m == -INFINITY) ? 0.f : m) - lse);
+            const char *np = rowp(nrow);
+            if constexpr (!kKeepExp)
+                opaque(buf, lse);
+            const uint32_t t1 = fresh_tid();  // indices not kept from pass 1
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const uint32_t v = tid + (uint32_t)i * BLOCK;
+                const uint32_t v = t1 + (uint32_t)i * BLOCK;
                 if (v < nvec) {
                     float x[N], g[N];
                     IO::unpack(buf[i], x);
@@ -346,6 +406,15 @@ struct RowKernel {
                         g[c] = kKeepExp ? x[c] * cf : coef * __expf(x[c] - lse);
                     store_vec(p, v, g, t, bm);
                 }
+                if constexpr (RL) {
+                    // Not before this vector's store: the register is the
+                    // one being freed (hoisted loads would need a second
+                    // row's worth of registers).
+                    __asm__ __volatile__("" ::: "memory");
+                    if (has_next)
+                        buf[i] = load_small(np, clamp_vec(v));
+                }
+                vector_fence();
             }
         } else {
             for (uint32_t v0 = tid; v0 < nvec; v0 += (uint32_t)BLOCK * U) {
@@ -395,7 +464,7 @@ struct RowKernel {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const uint32_t v = tid + (uint32_t)i * BLOCK;
-            load_to_lds16(p + (size_t)clamp_vec(v) * sizeof(Raw),
+            load_to_lds16(p + clamp_vec(v) * (uint32_t)sizeof(Raw),
                           pf + (uint32_t)i * BLOCK + (uint32_t)wid * kWave);
         }
     }
@@ -422,7 +491,7 @@ struct RowKernel {
                 prefetch_row(nrow);
         }
         fetch_targets(nrow, tn);
-        if constexpr (NV > 0 && !PF)
+        if constexpr (NV > 0 && !PF && !RL)
             load_row(rowp(row), cur);
         process(row, cur, tc, par, has_next, nrow, tn);
         par ^= 1;
@@ -449,6 +518,8 @@ struct RowKernel {
             fetch_targets(row, ta);
             if constexpr (NV > 0 && PF)
                 prefetch_row(row);
+            if constexpr (RL)
+                load_row(rowp(row), buf);
             gather_targets(row, ta, bitmaps);
             bool more = true;
             while (more) {
@@ -478,7 +549,7 @@ constexpr int min_waves_per_simd()
     return 1;
 }
 
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF>
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL>
 __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void row_loss_kernel(
     RowArgs a)
 {
@@ -488,7 +559,7 @@ __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void 
     __shared__ float sh_l[2][NW];
     // Dynamic LDS: [PF: BLOCK x NV 16-byte slots][KL: 2 x ceil(V/32) words]
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
-    using K = RowKernel<DT, KL, BLOCK, NV, VEC, PF>;
+    using K = RowKernel<DT, KL, BLOCK, NV, VEC, PF, RL>;
     constexpr uint32_t pf_words = PF ? (uint32_t)BLOCK * (NV > 0 ? NV : 1) * 4 : 0;
     K k(a, sh_m, sh_s, sh_l, dyn + pf_words, reinterpret_cast<typename K::Raw *>(dyn));
     k.run();
@@ -527,10 +598,10 @@ int cached_blocks_per_cu(const void *fn, int block, size_t lds)
     return nb;
 }
 
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false>
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false, bool RL = false>
 hipError_t launch_one(const RowArgs &a, hipStream_t st)
 {
-    auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF>;
+    auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF, RL>;
     size_t lds = 0;
     if (PF)
         lds += (size_t)BLOCK * (NV > 0 ? NV : 1) * 16;
@@ -589,6 +660,10 @@ hipError_t launch_dt(const RowArgs &a, hipStream_t st, bool vec)
             return launch_one<DT, KL, 256, 4, true>(a, st);
         if (nvec <= 4096)
             return launch_one<DT, KL, 512, 8, true, true>(a, st);
+        // One 1024-thread block per CU holds the whole row in registers and
+        // refills them with the next row as the gradient is stored.
+        if (nvec <= 1024 * 19)
+            return launch_one<DT, KL, 1024, 19, true, false, true>(a, st);
     }
     return launch_one<DT, KL, 1024, 0, true>(a, st);
 }
