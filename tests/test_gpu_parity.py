@@ -190,8 +190,8 @@ def test_kl_multirow(vl, dtype, V):
 
 # ------------------------------------------------------------ KL
 
-# (20000, 1500): float32 with the LDS prefetch leaves no room for the
-# teacher table, so the ids' own threads write the target entries.
+# (20000, 1500): more teacher ids than threads in the 512-thread float32
+# block with the LDS prefetch, so threads handle several ids each.
 KL_VK = [(1, 1), (8, 3), (512, 16), (1001, 64), (2049, 5), (8192, 128), (32000, 64),
          (20000, 1500), (32772, 200), (65544, 256), (131072, 2048), (151936, 256)]
 
