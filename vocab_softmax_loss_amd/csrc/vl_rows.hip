@@ -120,14 +120,17 @@ struct RowKernel {
         return *reinterpret_cast<const Raw *>(p + v * (uint32_t)sizeof(Raw));
     }
 
-    // The thread index as a value the compiler cannot see through: per-row
-    // index arithmetic is then redone per row (a few adds) instead of being
-    // hoisted out of the row loop and kept live, one register pair per
-    // vector, beside the row itself.
+    // RL: the thread index as a value the compiler cannot see through, so
+    // per-row index arithmetic is redone per row (a few adds) instead of
+    // being hoisted out of the row loop and kept live, one register pair
+    // per vector, beside a row that fills the registers.  Elsewhere the
+    // hoisting is cheaper than the recomputation (2.5 us on the 4096 x
+    // 32000 KL).
     __device__ uint32_t fresh_tid() const
     {
         uint32_t t = (uint32_t)tid;
-        __asm__ __volatile__("" : "+v"(t));
+        if constexpr (RL)
+            __asm__ __volatile__("" : "+v"(t));
         return t;
     }
 
