@@ -30,8 +30,19 @@ def dname(t):
     return "bf16" if t.dtype == torch.bfloat16 else "f32"
 
 
-def run_ce(vl, x, labels, rng, scale):
-    out = x.clone()
+def offset_rows(x):
+    """The same values in a row-major view whose base is one element past a
+    16-byte boundary: the 16-byte vector path cannot be used."""
+    n, V = x.shape
+    base = torch.empty(n * V + 1, dtype=x.dtype, device=x.device)
+    y = base[1:].view(n, V)
+    y.copy_(x)
+    assert y.data_ptr() % 16 != 0
+    return y
+
+
+def run_ce(vl, x, labels, rng, scale, misalign=False):
+    out = offset_rows(x) if misalign else x.clone()
     n = x.shape[0]
     loss = torch.full((n,), float("nan"), device=x.device)
     lse = torch.full((n,), float("nan"), device=x.device)
@@ -40,8 +51,8 @@ def run_ce(vl, x, labels, rng, scale):
     return loss.cpu().numpy(), lse.cpu().numpy(), to_host_bytes(out)
 
 
-def run_kl(vl, x, ids, probs, rng, coef):
-    out = x.clone()
+def run_kl(vl, x, ids, probs, rng, coef, misalign=False):
+    out = offset_rows(x) if misalign else x.clone()
     n = x.shape[0]
     loss = torch.full((n,), float("nan"), device=x.device)
     lse = torch.full((n,), float("nan"), device=x.device)
@@ -59,16 +70,16 @@ def run_topk(vl, x, k):
     return ids.cpu().numpy().view(np.uint32), probs.cpu().numpy()
 
 
-def assert_ce(vl, x, labels, rng, scale):
-    loss, lse, g = run_ce(vl, x, labels, rng, scale)
+def assert_ce(vl, x, labels, rng, scale, misalign=False):
+    loss, lse, g = run_ce(vl, x, labels, rng, scale, misalign)
     ol, olse, og = oracle.ce(to_host_bytes(x), labels.cpu().numpy(), rng=rng, scale=scale)
     check_loss(loss, ol, dname(x))
     check_loss(lse, olse, dname(x), "lse")
     check_grad(g, og, dname(x), scale)
 
 
-def assert_kl(vl, x, ids, probs, rng, coef):
-    loss, lse, g = run_kl(vl, x, ids, probs, rng, coef)
+def assert_kl(vl, x, ids, probs, rng, coef, misalign=False):
+    loss, lse, g = run_kl(vl, x, ids, probs, rng, coef, misalign)
     ol, olse, og = oracle.kl(to_host_bytes(x), ids.cpu().numpy(), probs.cpu().numpy(),
                              rng=rng, coef=coef)
     check_loss(loss, ol, dname(x))
@@ -193,7 +204,8 @@ def test_kl_multirow(vl, dtype, V):
 # (20000, 1500): more teacher ids than threads in the 512-thread float32
 # block with the LDS prefetch, so threads handle several ids each.
 KL_VK = [(1, 1), (8, 3), (512, 16), (1001, 64), (2049, 5), (8192, 128), (32000, 64),
-         (20000, 1500), (32772, 200), (65544, 256), (131072, 2048), (151936, 256)]
+         (20000, 1500), (32772, 200), (65544, 256), (131072, 2048), (151936, 256),
+         (1 << 19, 64)]  # the largest KL vocabulary: two 64 KB bitmaps in LDS
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -284,11 +296,38 @@ def test_topk_zipf_small(vl):
         check_topk(ids, probs, oi, op)
 
 
+def test_topk_long_rows(vl):
+    # 2^20 values per row: vector indices and ids past 2^18 and 2^20
+    x = gi.normal_logits(3, 1 << 20, 2.0, 78, DEV)
+    ids, probs = run_topk(vl, x, 100)
+    oi, op = oracle.topk(to_host_bytes(x), 100)
+    check_topk(ids, probs, oi, op)
+
+
 def test_topk_large_bf16_rows(vl):
     x = gi.normal_logits(8, 151936, 2.0, 77, DEV, torch.bfloat16)
     ids, probs = run_topk(vl, x, 256)
     oi, op = oracle.topk(to_host_bytes(x), 256)
     check_topk(ids, probs, oi, op)
+
+
+# ------------------------------------------------------------ misaligned rows
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["ce", "kl", "topk"])
+def test_misaligned_logits(vl, dtype, kind):
+    ntok, V, k = 40, 4096, 48
+    x = gi.normal_logits(ntok, V, 2.0, 31 + len(kind), DEV, TDT[dtype])
+    if kind == "ce":
+        assert_ce(vl, x, gi.uniform_labels(ntok, V, 32, DEV), (10, 2, 9), 1.0 / 28,
+                  misalign=True)
+    elif kind == "kl":
+        assert_kl(vl, x, gi.distinct_ids(ntok, V, k, 33, DEV),
+                  gi.softmax_probs(ntok, k, 1.5, 34, DEV), None, 0.25, misalign=True)
+    else:
+        ids, probs = run_topk(vl, offset_rows(x), k)
+        oi, op = oracle.topk(to_host_bytes(x), k)
+        check_topk(ids, probs, oi, op)
 
 
 # ------------------------------------------------------------ slice accumulate
