@@ -30,9 +30,10 @@
 // scanned across the wave with DPP.
 //
 // At the end the buffer is selected once more to exactly k winners, which
-// a register bitonic sort on (key, complemented id) puts in output order
-// (lanes exchange entries with ds_bpermute); the probabilities are formed
-// from the winners' values.
+// a bitonic sort on (key, complemented id) puts in output order: in
+// registers up to 512 winners (lanes exchange entries with ds_bpermute),
+// in the LDS buffer beyond; the probabilities are formed from the winners'
+// values.
 #include <math.h>
 
 #include "vl_device.hpp"
@@ -301,13 +302,60 @@ __device__ __forceinline__ void write_ranked(const uint32_t *keys, const uint32_
 // VGPRs): the 1024-entry bf16 variant would otherwise take 138 and run three
 // waves per SIMD, 11% slower at 16384 x 151936 despite a few spilled
 // registers in its compaction.
+// Above 512 winners the register sort would need 16+ register pairs per
+// lane; the k winners are sorted in place in the LDS buffer instead, by the
+// same bitonic network over P = the power of two >= k entries (CAP >= P
+// because CAP >= k + one sub-tile).  keys/ids[k..P) are padded with the
+// pair that sorts last.
+__device__ __forceinline__ void write_ranked_lds(uint32_t *keys, uint32_t *ids, int k, uint32_t *out_ids,
+                                                 float *out_p)
+{
+    const int lane = lane_id();
+    int P = kWave;
+    while (P < k)
+        P <<= 1;
+    for (int i = k + lane; i < P; i += kWave) {
+        keys[i] = 0u;
+        ids[i] = 0xFFFFFFFFu;
+    }
+    wave_lds_sync();
+    for (int kk = 2; kk <= P; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            // pair number pp: lower index i, partner i + j
+            for (int pp = lane; pp < P / 2; pp += kWave) {
+                const int i = 2 * j * (pp / j) + pp % j;
+                const int l = i + j;
+                const uint64_t a = sort_pair(keys[i], ids[i]);
+                const uint64_t b = sort_pair(keys[l], ids[l]);
+                const bool desc = (i & kk) == 0;
+                if (desc ? a < b : a > b) {
+                    keys[i] = (uint32_t)(b >> 32);
+                    ids[i] = ~(uint32_t)b;
+                    keys[l] = (uint32_t)(a >> 32);
+                    ids[l] = ~(uint32_t)a;
+                }
+            }
+            wave_lds_sync();
+        }
+    }
+    const float v0 = key_value(keys[0]);
+    float z = 0.f;
+    for (int i = lane; i < k; i += kWave)
+        z += __expf(key_value(keys[i]) - v0);
+    const float Z = wave_sum(z);
+    for (int i = lane; i < k; i += kWave) {
+        out_ids[i] = ids[i];
+        out_p[i] = __expf(key_value(keys[i]) - v0) / Z;
+    }
+}
+
 template <int DT, bool VEC, int CAP, int WPB>
 __global__ __launch_bounds__(WPB * kWave, (CAP <= 1024 ? 4 : 1)) void topk_kernel(TopkArgs a)
 {
     using IO = RowIO<DT, VEC>;
     using Raw = typename IO::Raw;
     constexpr int N = IO::N;
-    constexpr int U = (N == 1) ? 16 : 4;
+    constexpr int U = 4;
     constexpr int SUB = kWave * N;  // elements per sub-tile
     constexpr int E = CAP / kWave;
     // k <= min(CAP - SUB, kMaxTopk); the sort pads k to a power of two.
@@ -442,7 +490,10 @@ __global__ __launch_bounds__(WPB * kWave, (CAP <= 1024 ? 4 : 1)) void topk_kerne
     // exactly k winners, in id order, then written at their ranks
     wave_lds_sync();
     select_compact<E>(keys, ids, cnt, k, hist);  // leaves exactly k entries
-    write_ranked<kSortRegs>(keys, ids, k, a.ids + row * a.k, a.probs + row * a.k);
+    if constexpr (kSortRegs <= 8)
+        write_ranked<kSortRegs>(keys, ids, k, a.ids + row * a.k, a.probs + row * a.k);
+    else
+        write_ranked_lds(keys, ids, k, a.ids + row * a.k, a.probs + row * a.k);
 }
 
 namespace {
