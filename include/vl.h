@@ -106,7 +106,7 @@ int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *pro
  *           descending, id ascending); -0 and +0 tie.
  *   probs   [ntok][k] float32, written: exp(v_q - v_0) / sum_{q<k} exp(v_q - v_0)
  *           in the same order (the softmax restricted to the k).
- * Limits: 1 <= k <= min(V, 2048), V <= 2^31 - 1.
+ * Limits: 1 <= k <= min(V, 2048), V <= 2^31 - 1, ntok <= 2^31 - 1.
  */
 int vl_topk_renorm(const void *logits, int dtype, int64_t ntok, int64_t V, int64_t k,
                    uint32_t *ids, float *probs, hipStream_t stream);

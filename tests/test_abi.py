@@ -107,6 +107,7 @@ def test_topk_host_checks(lib):
     assert f(P, 0, 4, 5000, 2049, P, P, None) == VL_EINVAL  # k > 2048
     assert f(P, 0, 4, 0, 1, P, P, None) == VL_EINVAL
     assert f(P, 0, -1, 10, 2, P, P, None) == VL_EINVAL
+    assert f(P, 0, 1 << 31, 4, 2, P, P, None) == VL_EINVAL  # more rows than workgroups
     assert f(None, 0, 4, 10, 2, P, P, None) == VL_EINVAL
     assert f(P, 0, 4, 10, 2, None, P, None) == VL_EINVAL
     assert f(P, 0, 4, 10, 2, P, None, None) == VL_EINVAL

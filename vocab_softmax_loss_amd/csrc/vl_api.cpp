@@ -117,7 +117,8 @@ int vl_topk_renorm(const void *logits, int dtype, int64_t ntok, int64_t V, int64
 {
     if (bad_dtype(dtype))
         return VL_EDTYPE;
-    if (ntok < 0 || V < 1 || V > kMaxV || k < 1 || k > V || k > vl::kMaxTopk)
+    // one wave per row: the grid holds at most 2^31 - 1 workgroups
+    if (ntok < 0 || ntok > kMaxV || V < 1 || V > kMaxV || k < 1 || k > V || k > vl::kMaxTopk)
         return VL_EINVAL;
     if (ntok > INT64_MAX / V)
         return VL_EINVAL;
