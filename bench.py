@@ -145,7 +145,9 @@ def other_workload(name, dev):
         k = c["ids"].shape[1]
         loss = torch.empty(ntok, device=dev)
         calls = [("kl", lambda: vl.vl_kl_fwd_bwd(x, c["ids"], c["probs"], loss, coef=c["coef"]))]
-        # online variant: the row is read twice and written once
+        # online variant: the method reads the row twice and writes it once
+        # (part of the second read is served from LDS and the Infinity
+        # Cache, so the rate under this count can exceed what HBM moves)
         nbytes = {"kl": ntok * 3 * V * 4 + ntok * k * 8 + ntok * 4}
         cfg = {"workload": gi.KL_LARGE.name, "ntok": ntok, "V": V, "k": k, "dtype": "f32",
                "bytes_model": "2R+1W"}

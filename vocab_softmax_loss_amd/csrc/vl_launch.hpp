@@ -88,6 +88,7 @@ struct RowArgs {
     int64_t ntok, V, k;
     RowWalk walk;             // loss range as a row order
     float coef;               // gradient scale
+    int64_t lds_vecs;         // online: leading vectors of a row kept in LDS for pass 2
 };
 
 struct TopkArgs {

@@ -92,6 +92,10 @@ struct RowKernel {
     float (*sh_l)[NW];
     uint32_t *bitmaps;
     Raw *pf;  // PF: BLOCK x NB vectors, slot v holds vector v of the next row
+    // Online: slot v < nlds holds vector v of the current row from pass 1
+    // until pass 2 reads it (each slot is written and read by one thread).
+    Raw *lrow;
+    uint32_t nlds;
     const int tid, wid, lane, words;
     const uint32_t V, nvec, k;
     const float coef;
@@ -103,6 +107,8 @@ struct RowKernel {
           V((uint32_t)args.V), nvec((uint32_t)(args.V / IO::N)), k((uint32_t)args.k),
           coef(args.coef)
     {
+        lrow = reinterpret_cast<Raw *>(bm + (KL ? ((2 * words + 3) & ~3) : 0));
+        nlds = (uint32_t)args.lds_vecs;
     }
 
     __device__ char *rowp(int64_t row) const
@@ -290,6 +296,11 @@ struct RowKernel {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     y[u] = IO::load_raw(p, clamp_vec(v0 + (uint32_t)u * BLOCK));
+                // nlds is a multiple of BLOCK: each test is uniform
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (v0 + (uint32_t)u * BLOCK < nlds)
+                        lrow[v0 + (uint32_t)u * BLOCK] = y[u];
                 float cm = -INFINITY;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -423,8 +434,10 @@ struct RowKernel {
             for (uint32_t v0 = tid; v0 < nvec; v0 += (uint32_t)BLOCK * U) {
                 Raw y[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    y[u] = IO::load_raw(p, clamp_vec(v0 + (uint32_t)u * BLOCK));
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t v = v0 + (uint32_t)u * BLOCK;
+                    y[u] = v < nlds ? lrow[v] : IO::load_raw(p, clamp_vec(v));
+                }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const uint32_t v = v0 + (uint32_t)u * BLOCK;
@@ -572,6 +585,10 @@ __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void 
 
 namespace {
 
+// Dynamic LDS a block may take: 160 KB per CU on gfx950, less a margin for
+// the kernel's static arrays (under 1 KB).
+constexpr size_t kMaxDynLds = 160 * 1024 - 1024;
+
 struct OccKey {
     const void *fn;
     size_t lds;
@@ -605,11 +622,26 @@ template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false, bool RL
 hipError_t launch_one(const RowArgs &a, hipStream_t st)
 {
     auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF, RL>;
+    RowArgs args = a;
     size_t lds = 0;
     if (PF)
         lds += (size_t)BLOCK * (NV > 0 ? NV : 1) * 16;
     if (KL)
-        lds += 2 * (size_t)((a.V + 31) >> 5) * sizeof(uint32_t);
+        lds += ((2 * (size_t)((a.V + 31) >> 5) + 3) & ~size_t(3)) * sizeof(uint32_t);
+    args.lds_vecs = 0;
+    if (NV == 0) {
+        // Online: the rest of LDS keeps the row's leading vectors, in units
+        // of BLOCK, for pass 2, which reads them from there instead of HBM.
+        // Those are the first read in pass 1, the least likely to be still
+        // cached.
+        const size_t unit = (size_t)BLOCK * sizeof(typename RowIO<DT, VEC>::Raw);
+        const size_t room = lds < kMaxDynLds ? (kMaxDynLds - lds) / unit : 0;
+        const int64_t nvec = a.V / RowIO<DT, VEC>::N;
+        const int64_t units = (nvec + BLOCK - 1) / BLOCK;
+        const int64_t keep = (int64_t)room < units ? (int64_t)room : units;
+        args.lds_vecs = keep * BLOCK;
+        lds += (size_t)keep * unit;
+    }
     {
         if (lds > 65536) {
             hipError_t e = hipFuncSetAttribute((const void *)fn,
@@ -626,7 +658,7 @@ hipError_t launch_one(const RowArgs &a, hipStream_t st)
     int64_t grid = (int64_t)per_cu * device_cus();
     if (grid > rows)
         grid = rows;
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(BLOCK), lds, st, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(BLOCK), lds, st, args);
     return hipGetLastError();
 }
 
