@@ -209,6 +209,31 @@ KL_VK = [(1, 1), (8, 3), (512, 16), (1001, 64), (2049, 5), (8192, 128), (32000, 
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [4096, 32000, 40008])
+def test_kl_clustered_ids(vl, dtype, V):
+    """Teacher ids packed into few 16-byte vectors (1 to 8 targets per
+    vector), beside vectors holding a single one: both ways of writing the
+    target entries, in the staged, prefetched, online and register-refill
+    variants."""
+    ntok, k = 300, 40
+    g = torch.Generator()
+    g.manual_seed(V)
+    rows = []
+    for r in range(ntok):
+        base = torch.randperm(V // 8, generator=g)[:26] * 8
+        single = base[4:] + (r + torch.arange(22)) % 8  # one target in each
+        rows.append(torch.cat([base[0] + torch.arange(8), base[1] + torch.arange(5),
+                               base[2] + torch.tensor([0, 7]),
+                               base[3] + torch.tensor([2, 3, 4]), single]))
+    ids = torch.stack([x[torch.randperm(k, generator=g)] for x in rows]).to(torch.int32)
+    assert ids.shape == (ntok, k) and all(torch.unique(x).numel() == k for x in ids)
+    ids = ids.to(DEV)
+    x = gi.normal_logits(ntok, V, 2.0, 1100 + V, DEV, TDT[dtype])
+    probs = gi.softmax_probs(ntok, k, 1.5, 1200 + V, DEV)
+    assert_kl(vl, x, ids, probs, None, 1024.0 / ntok)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V,k", KL_VK)
 def test_kl_shapes(vl, dtype, V, k):
     ntok = 6

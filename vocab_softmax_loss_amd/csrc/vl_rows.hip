@@ -38,8 +38,11 @@
 //
 // Targets.  CE: the thread that owns the label's vector subtracts coef from
 // that element before its store.  KL: the teacher ids of the row are marked
-// in an LDS bitmap of V bits; the bulk store skips marked elements, and the
-// thread that handles id q writes coef (p_id - p_q) there itself, so every
+// in an LDS bitmap of V bits and the bulk store skips every vector holding
+// one.  The thread that handles id q writes coef (p_id - p_q) there: if it
+// is its vector's only mark, it reads that vector's logits back (nothing
+// has overwritten them) and writes the whole vector; otherwise the owner
+// writes the vector's unmarked elements one by one and q its own.  Every
 // element has exactly one writer (no read-modify-write of the gradient).
 // The two bitmaps alternate by row parity and are cleared one row late.
 // The label (scalar load), ids and probs of the next row are fetched ahead,
@@ -237,7 +240,7 @@ struct RowKernel {
             const uint32_t bits = (bm[j0 >> 5] >> (j0 & 31)) & (uint32_t)((1ull << N) - 1);
             if (bits == 0u) {
                 IO::store(q, vi, g);
-            } else {
+            } else if (__builtin_popcount(bits) > 1) {  // one target: its thread writes it all
 #pragma unroll
                 for (int c = 0; c < N; ++c)
                     if (!((bits >> c) & 1u))
@@ -383,7 +386,24 @@ struct RowKernel {
                 const float d = (sv - M) - logS;  // log p_S at the id
                 if (pq > 0.f)
                     acc += pq * (__logf(pq) - d);
-                IO::store_elem(p, id, coef * (__expf(d) - pq));
+                const float gid = coef * (__expf(d) - pq);
+                if constexpr (N > 1) {
+                    const uint32_t v = id / N, j0 = v * N;
+                    const uint32_t vb = (bm[j0 >> 5] >> (j0 & 31)) & (uint32_t)((1ull << N) - 1);
+                    if (__builtin_popcount(vb) == 1) {
+                        // The vector's only target: this thread writes the
+                        // whole vector (its owner skips it), from the row's
+                        // values, which nothing has overwritten.
+                        float x[N], g[N];
+                        IO::unpack(IO::load_raw(p, v), x);
+#pragma unroll
+                        for (int c = 0; c < N; ++c)
+                            g[c] = (uint32_t)c == id - j0 ? gid : coef * __expf(x[c] - lse);
+                        IO::store(p, v, g);
+                        continue;
+                    }
+                }
+                IO::store_elem(p, id, gid);
             }
             const float wl = wave_sum(acc);
             if (lane == 0)
