@@ -204,22 +204,27 @@ struct RowKernel {
         t.s = 0.f;
     }
 
-    // Once the previous row is stored: the logits at the targets and, for
-    // KL, the row's marks in bitmap `bm` (cleared by then).
-    __device__ void gather_targets(int64_t row, Tgt &t, uint32_t *bm) const
+    // The logit at the label (CE) or at this thread's teacher id (KL).
+    __device__ void gather_s(int64_t row, Tgt &t) const
     {
         const char *p = rowp(row);
         if constexpr (!KL) {
             if (tid == 0 && t.label < V)
                 t.s = IO::load_elem(p, t.label);
         } else {
+            if ((uint32_t)tid < k && t.id < V)
+                t.s = IO::load_elem(p, t.id);
+        }
+    }
+
+    // KL: the row's marks in bitmap `bm` (cleared by then).
+    __device__ void mark_targets(int64_t row, const Tgt &t, uint32_t *bm) const
+    {
+        if constexpr (KL) {
             for (uint32_t q = tid; q < k; q += BLOCK) {
                 const uint32_t id = q == (uint32_t)tid ? t.id : a.ids[row * k + q];
-                if (id < V) {
+                if (id < V)
                     atomicOr(&bm[id >> 5], 1u << (id & 31));
-                    if (q == (uint32_t)tid)
-                        t.s = IO::load_elem(p, id);
-                }
             }
         }
     }
@@ -473,8 +478,10 @@ struct RowKernel {
             }
         }
 
-        if (has_next)
-            gather_targets(nrow, tn, bm_other);
+        if (has_next) {
+            mark_targets(nrow, tn, bm_other);
+            gather_s(nrow, tn);
+        }
     }
 
     __device__ void zero_row(int64_t row) const
@@ -509,6 +516,8 @@ struct RowKernel {
     // from this lane's LDS slots (filled during the previous step) and the
     // next row's loads are issued into them; without PF it is loaded here.
     // Returns whether a next row exists.
+    // One row; tc holds its targets and receives the next row's, which
+    // are fetched into tn.
     __device__ bool step(RowCursor &cur_pos, int64_t &row, Raw (&cur)[NB], Tgt &tc, Tgt &tn,
                          int &par) const
     {
@@ -533,6 +542,7 @@ struct RowKernel {
         par ^= 1;
         cur_pos = nc;
         row = nrow;
+        tc = tn;
         return has_next;
     }
 
@@ -556,13 +566,9 @@ struct RowKernel {
                 prefetch_row(row);
             if constexpr (RL)
                 load_row(rowp(row), buf);
-            gather_targets(row, ta, bitmaps);
-            bool more = true;
-            while (more) {
-                more = step(c, row, buf, ta, tb, par);
-                if (!more)
-                    break;
-                more = step(c, row, buf, tb, ta, par);
+            mark_targets(row, ta, bitmaps);
+            gather_s(row, ta);
+            while (step(c, row, buf, ta, tb, par)) {
             }
         }
         RowCursor o;
