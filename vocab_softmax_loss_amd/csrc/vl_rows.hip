@@ -28,9 +28,11 @@
 //    exp(m_thread - lse): one exp per element.
 //  * online (NV == 0): the row is streamed twice: pass 1 keeps a running
 //    (max, sum) per thread with one rescale per chunk, pass 2 writes the
-//    gradient (2R + 1W).  One 1024-thread block per CU keeps the rows in
-//    flight small enough for the second pass to find them in the
-//    Infinity Cache.
+//    gradient (2R + 1W).  The row's leading vectors, as many as the
+//    block's spare LDS holds, are kept there by pass 1 for pass 2; one
+//    1024-thread block per CU keeps the rows in flight small enough for
+//    the rest of the second pass to find much of them in the Infinity
+//    Cache.
 // (max, sum) pairs reduce across the wave with DPP and across waves through
 // LDS, one barrier per row (an LDS-only barrier: it does not wait for the
 // prefetched loads); the LDS slots alternate by row parity so a fast wave

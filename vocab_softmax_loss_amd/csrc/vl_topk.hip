@@ -8,19 +8,20 @@
 // candidates; that is exact only while no thread sees more than 8 of the
 // true top-k.  This kernel is exact for every input:
 //
-// One wave owns a row and streams it once, in tiles of 64 lanes x U
+// One wave owns a row and streams it once, in tiles of 64 lanes x 4
 // 16-byte vectors (the next tile's loads in flight while one is filtered);
 // a tile's ids are all larger than every earlier tile's.  Values pass an
 // acceptance test into a per-wave LDS candidate buffer of (key, id) pairs,
 // written in id order.  The key is the order-preserving unsigned image of
 // the float (sign-flipped, -0 folded onto +0), so key order is value order.
 // Until the buffer first fills every value is accepted; when a sub-tile
-// might overflow it, the buffer is compacted to its own top-k: an exact
-// select on the keys, then the keys above the k-th key and, of those equal
-// to it, the first ones in buffer (= id) order.  The k-th key becomes the
-// threshold: later elements have larger ids, so only values strictly above
-// it can enter the top-k, and a per-vector max test skips almost every
-// sub-tile.
+// might overflow it, the buffer is compacted.  Mid-row that keeps every key
+// at or above a bound that at least k keys reach (the first radix bin edge
+// that keeps few enough); at the end it is exact: the keys above the k-th
+// key and, of those equal to it, the first ones in buffer (= id) order.
+// The bound becomes the threshold: later elements have larger ids, so only
+// values strictly above it can enter the top-k, and a test of each lane's
+// largest value skips the sub-tiles no value of which can.
 //
 // The select holds the candidates in registers and is a radix select on
 // key - min(key) over the buffer: 8-bit digits from the highest set bit of
