@@ -50,6 +50,11 @@ def _load():
             lib.oracle_ce.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, i64, i64,
                                       i64, dbl, vp, vp, vp]
             lib.oracle_ce.restype = None
+            lib.oracle_ce_bwd.argtypes = [vp, ctypes.c_int, vp, vp, i64, i64, vp, i64, i64,
+                                          i64, dbl, vp]
+            lib.oracle_ce_bwd.restype = None
+            lib.oracle_loss_mean.argtypes = [vp, i64, i64, i64, i64]
+            lib.oracle_loss_mean.restype = dbl
             lib.oracle_kl.argtypes = [vp, ctypes.c_int, vp, vp, i64, i64, i64, vp,
                                       i64, i64, i64, dbl, vp, vp, vp]
             lib.oracle_kl.restype = None
@@ -106,6 +111,28 @@ def ce(logits, labels, rng=None, scale=1.0, row_index=None, want_grad=True):
     _load().oracle_ce(_ptr(a), _dtype_code(a), _ptr(lab), n, V, _ptr(ridx), sl, st, en,
                       float(scale), _ptr(loss), _ptr(lse), _ptr(grad))
     return loss, lse, grad
+
+
+def ce_bwd(logits, labels, lse, rng=None, scale=1.0, row_index=None):
+    """float64 gradient from a saved float32 logsumexp per row."""
+    a = _rows2d(logits)
+    n, V = a.shape
+    lab = np.ascontiguousarray(labels).astype(np.uint32, copy=False).reshape(-1)
+    L = np.ascontiguousarray(lse, dtype=np.float32).reshape(-1)
+    assert lab.size == n and L.size == n
+    ridx = None if row_index is None else np.ascontiguousarray(row_index, dtype=np.int64)
+    grad = np.empty((n, V))
+    sl, st, en = _range_args(rng)
+    _load().oracle_ce_bwd(_ptr(a), _dtype_code(a), _ptr(lab), _ptr(L), n, V, _ptr(ridx), sl,
+                          st, en, float(scale), _ptr(grad))
+    return grad
+
+
+def loss_mean(loss, rng=None):
+    """Mean of a float32 loss vector over the loss range, as float64."""
+    x = np.ascontiguousarray(loss, dtype=np.float32).reshape(-1)
+    sl, st, en = _range_args(rng)
+    return _load().oracle_loss_mean(_ptr(x), x.size, sl, st, en)
 
 
 def kl(logits, ids, probs, rng=None, coef=1.0, row_index=None, want_grad=True):

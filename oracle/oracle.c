@@ -19,7 +19,8 @@
  *   [CE]  aprender-train 0.36.0, entrenar/autograd/wgpu_cross_entropy.rs:
  *         module doc (forward and backward formulas), CEForwardParams and
  *         CEBackwardParams (the loss range and scale), read_loss (the mean
- *         over the loss range), backward (gradient written in place).
+ *         over the loss range), forward_async (loss and logsumexp per row),
+ *         backward (gradient written in place from the saved logsumexp).
  *   [KL]  cortiq-engine 0.8.21, src/gpu_wgpu/train_head.rs: module doc (the
  *         distillation loss and its gradient), the kl_rows kernel, the
  *         topk_rows kernel (teacher top-k with probabilities renormalised
@@ -121,6 +122,54 @@ void oracle_ce(const void *logits, int dtype, const uint32_t *labels,
                 g[j] = scale * (exp(widen(row, dtype, j) - L) - onehot);
             }
     }
+}
+
+/*
+ * Cross-entropy backward from a saved logsumexp [CE: backward, which takes
+ * the logsumexp the forward pass stored instead of reducing the row again]:
+ *   grad_rj = scale * (exp(s_j - lse_r) - [j == label])
+ * lse_r is the given float32 value, widened exactly and used as given.
+ * Rows outside the loss range get gradient 0, as in oracle_ce.
+ */
+void oracle_ce_bwd(const void *logits, int dtype, const uint32_t *labels, const float *lse,
+                   int64_t nrows, int64_t V, const int64_t *row_index, int64_t seq_len,
+                   int64_t start, int64_t end, double scale, double *grad)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+        const void *row = row_ptr(logits, dtype, i, V);
+        int64_t r = row_index ? row_index[i] : i;
+        double *g = grad + i * V;
+        if (!in_loss(r, seq_len, start, end)) {
+            for (int64_t j = 0; j < V; ++j)
+                g[j] = 0.0;
+            continue;
+        }
+        double L = (double)lse[i];
+        int64_t label = (int64_t)labels[i];
+        for (int64_t j = 0; j < V; ++j) {
+            double onehot = (j == label) ? 1.0 : 0.0;
+            g[j] = scale * (exp(widen(row, dtype, j) - L) - onehot);
+        }
+    }
+}
+
+/*
+ * Mean loss [CE: read_loss]: the sum of the loss over every row (rows
+ * outside the range hold 0 after the forward) divided by the number of rows
+ * in the loss range, or 0 when the range holds no row.  Summed in index
+ * order.
+ */
+double oracle_loss_mean(const float *loss, int64_t nrows, int64_t seq_len, int64_t start,
+                        int64_t end)
+{
+    double sum = 0.0;
+    int64_t count = 0;
+    for (int64_t i = 0; i < nrows; ++i) {
+        sum += (double)loss[i];
+        count += in_loss(i, seq_len, start, end);
+    }
+    return count > 0 ? sum / (double)count : 0.0;
 }
 
 /*

@@ -176,6 +176,86 @@ def test_ce_page_test_mean_loss():
     assert abs(loss.sum() / 4 - float(cpu)) < 1e-4
 
 
+# ------------------------------------------- CE split: backward from lse, mean
+
+def test_ce_bwd_constant_rows_closed_form():
+    """Row r constant c_r with its saved lse c_r + ln V (rounded to float32):
+    every softmax entry is 1/V, so g = scale (1/V - [j = label]).  The rows
+    differ, so a logsumexp taken from the wrong row fails."""
+    V, n = 16, 6
+    c = np.array([-3.0, -1.5, 0.0, 0.75, 2.0, 5.5], dtype=np.float32)
+    x = np.repeat(c[:, None], V, axis=1)
+    lab = np.array([0, 3, 15, 7, 1, 9])
+    lse = (c.astype(np.float64) + math.log(V)).astype(np.float32)
+    g = oracle.ce_bwd(x, lab, lse, scale=0.25)
+    want = np.full((n, V), 0.25 / V)
+    want[np.arange(n), lab] -= 0.25
+    # lse is float32: p = exp(c - fl(c + ln V)) = (1/V)(1 + O(2^-24 |lse|))
+    np.testing.assert_allclose(g, want, rtol=0, atol=0.25 / V * 1e-6)
+
+
+def test_ce_bwd_matches_scipy_softmax():
+    """With the correctly rounded float32 logsumexp of each row (scipy), the
+    gradient is scale (softmax(row) - one_hot) from scipy, up to that
+    rounding."""
+    x = rows_f32(5, 3000)
+    lab = RNG.integers(0, 3000, size=5)
+    lse64 = scipy.special.logsumexp(x.astype(np.float64), axis=1)
+    g = oracle.ce_bwd(x, lab, lse64.astype(np.float32), scale=0.5)
+    sm = scipy.special.softmax(x.astype(np.float64), axis=1)
+    sm[np.arange(5), lab] -= 1.0
+    err = np.abs(g - 0.5 * sm)
+    tol = 0.5 * np.abs(sm) * (np.abs(lse64)[:, None] * 2.0**-23 + 1e-14)
+    assert (err <= tol + 1e-300).all()
+
+
+def test_ce_bwd_lse_shift_scales_softmax_part():
+    """Raising the saved lse by 1 divides the softmax part exp(s - lse) by e
+    and leaves the one-hot part: g + scale onehot scales by exp(-1)."""
+    x = rows_f32(3, 200)
+    lab = np.array([5, 0, 199])
+    lse = np.array([2.5, -1.0, 7.0], dtype=np.float32)  # lse + 1 exact in float32
+    g0 = oracle.ce_bwd(x, lab, lse, scale=2.0)
+    g1 = oracle.ce_bwd(x, lab, lse + np.float32(1.0), scale=2.0)
+    oh = np.zeros_like(g0)
+    oh[np.arange(3), lab] = 2.0
+    # adding the one-hot back at the label cancels: one ulp of scale absolute
+    np.testing.assert_allclose(g1 + oh, (g0 + oh) * math.exp(-1.0), rtol=1e-14,
+                               atol=2.0 * 2.0**-52)
+
+
+def test_ce_bwd_range_and_bf16():
+    """Rows outside the range are zero; bf16 rows are read through the exact
+    widening (same result as their float32 widening)."""
+    x = rows_f32(10, 64)
+    b = f32_to_bf16_bits(x)
+    xw = bf16_bits_to_f64(b).astype(np.float32)
+    lab = RNG.integers(0, 64, size=10)
+    lse = np.linspace(1.0, 4.0, 10).astype(np.float32)
+    rng = (4, 1, 3)
+    gb = oracle.ce_bwd(b, lab, lse, rng=rng, scale=1.0)
+    gw = oracle.ce_bwd(xw, lab, lse, rng=rng, scale=1.0)
+    assert np.array_equal(gb, gw)
+    for r in range(10):
+        if 1 <= r % 4 < 3:
+            assert gb[r].any()
+        else:
+            assert not gb[r].any()
+
+
+def test_loss_mean_hand_cases():
+    """The mean loss sums every row and divides by the rows in the range
+    (read_loss); values worked by hand."""
+    l8 = np.arange(1, 9, dtype=np.float32)  # sum 36
+    assert oracle.loss_mean(l8) == 4.5
+    assert oracle.loss_mean(l8, (4, 1, 3)) == 9.0     # rows 1, 2, 5, 6 in range
+    assert oracle.loss_mean(l8, (8, 2, 5)) == 12.0    # rows 2, 3, 4
+    assert oracle.loss_mean(l8, (8, 3, 3)) == 0.0     # empty range
+    l10 = np.arange(1, 11, dtype=np.float32)  # sum 55; rows 1, 2, 5, 6, 9
+    assert oracle.loss_mean(l10, (4, 1, 3)) == 11.0
+    assert oracle.loss_mean(np.zeros(0, dtype=np.float32)) == 0.0
+
+
 # ----------------------------------------------------------------- KL
 
 def renorm_probs(n, k, sigma=1.5, rng=RNG):
