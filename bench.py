@@ -18,7 +18,7 @@ Prints one JSON line.  `value` is logits rows per second of the whole step;
 the launch stream around every launch of the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-                    [--workload step|ce_lm|topk_zipf|kl_large|kl_bf16|copy_calib]
+                    [--workload step|ce_lm|ce_split|topk_zipf|kl_large|kl_bf16|copy_calib]
     python bench.py --pmc-summary <counter_collection.csv> ...
 
 The other workloads time one configuration each at its full size, for
@@ -129,6 +129,24 @@ def other_workload(name, dev):
                                                  scale=c["scale"]))]
         nbytes = {"ce": n_in * 2 * V * 4 + (ntok - n_in) * V * 4 + ntok * 8}
         cfg = {"workload": gi.CE_LM.name, "ntok": ntok, "V": V, "dtype": "f32"}
+    elif name == "ce_split":
+        # the same configuration through the two-pass calls: forward only,
+        # backward from the saved lse, then the mean loss on the device
+        c = gi.ce_lm(dev)
+        x, lab, rng = c["logits"], c["labels"], c["rng"]
+        ntok, V = x.shape
+        loss = torch.empty(ntok, device=dev)
+        lse = torch.empty(ntok, device=dev)
+        mean = torch.empty(1, device=dev)
+        n_in = 8 * 384
+        calls = [("ce_fwd", lambda: vl.vl_ce_fwd(x, lab, loss, lse, rng=rng)),
+                 ("ce_bwd", lambda: vl.vl_ce_bwd(x, lab, lse, rng=rng, scale=c["scale"])),
+                 ("mean", lambda: vl.vl_loss_mean(loss, mean, rng=rng))]
+        nbytes = {"ce_fwd": n_in * V * 4 + n_in * 4 + ntok * 8,
+                  "ce_bwd": n_in * 2 * V * 4 + (ntok - n_in) * V * 4 + n_in * 8,
+                  "mean": ntok * 4 + 4}
+        cfg = {"workload": gi.CE_LM.name + ", two-pass calls", "ntok": ntok, "V": V,
+               "dtype": "f32", "bytes_model": "forward 1R, backward 1R+1W"}
     elif name == "topk_zipf":
         c = gi.topk_zipf(dev)
         t, k = c["teacher"], c["k"]

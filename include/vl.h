@@ -6,8 +6,9 @@
  *   [CE] aprender-train 0.36.0, entrenar/autograd/wgpu_cross_entropy.rs:
  *        module doc (loss = logsumexp(logits) - logits[label]; gradient
  *        softmax - one_hot(label), written in place), CEForwardParams /
- *        CEBackwardParams (loss range, scale), backward (scaled in-place
- *        gradient), read_loss (mean over the loss range, taken by the caller).
+ *        CEBackwardParams (loss range, scale), forward_async (loss and
+ *        logsumexp per row), backward (scaled in-place gradient from the
+ *        saved logsumexp), read_loss (mean over the loss range).
  *   [KL] cortiq-engine 0.8.21, src/gpu_wgpu/train_head.rs: module doc
  *        (distillation KL against the teacher's renormalised top-k and its
  *        gradient p_S - p_T, written in place and scaled), kl_rows, topk_rows
@@ -24,7 +25,8 @@
  *     input and output.
  *   - Returns VL_OK (0) or a negative status; vl_strerror names it.  Invalid
  *     sizes, dtypes and null pointers are rejected on the host before any
- *     GPU work.  ntok == 0 (or n == 0) is a no-op that returns VL_OK.
+ *     GPU work.  ntok == 0 (or n == 0) is a no-op that returns VL_OK
+ *     (except vl_loss_mean, which still writes its result).
  *   - Preconditions NOT checked on the device: label < V; ids < V and
  *     distinct within a row; probs >= 0; logits free of NaN and +inf with at
  *     least one finite value per row.  Violating them never faults: a label
@@ -81,6 +83,52 @@ enum {
 int vl_ce_fwd_bwd(void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
                   int64_t ntok, int64_t V, const vl_range *rng, float scale,
                   hipStream_t stream);
+
+/*
+ * Cross-entropy forward only [CE: forward_async, which stores the per-row
+ * loss and logsumexp for a later backward and reads nothing back].
+ *   logits  [ntok][V] dtype, read only.
+ *   labels  [ntok] uint32, read only.
+ *   loss    [ntok] float32, written: logsumexp(row) - row[label], unscaled.
+ *   lse     [ntok] float32 or NULL, written: logsumexp(row), the input of
+ *           vl_ce_bwd.
+ *   rng     loss range or NULL.  Rows outside it are not read; their loss
+ *           and lse are 0.
+ * loss and lse may differ from vl_ce_fwd_bwd's in the last bits: the two
+ * reduce the row in different orders.
+ * Limits: as vl_ce_fwd_bwd.
+ */
+int vl_ce_fwd(const void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
+              int64_t ntok, int64_t V, const vl_range *rng, hipStream_t stream);
+
+/*
+ * Cross-entropy backward from a saved logsumexp [CE: backward].
+ *   logits  [ntok][V] dtype, in: the logits; out: the gradient
+ *           scale * (exp(row - lse) - one_hot(label)), stored in dtype.
+ *   labels  [ntok] uint32, read only.
+ *   lse     [ntok] float32, read only: logsumexp of each row, as vl_ce_fwd
+ *           wrote it; used as given.
+ *   rng     loss range or NULL.  Rows outside it are not read and their
+ *           gradient row is set to 0; their lse is not read either.
+ *   scale   gradient scale, e.g. 1 / (rows in the range) for the mean loss.
+ * Limits: as vl_ce_fwd_bwd.
+ */
+int vl_ce_bwd(void *logits, int dtype, const uint32_t *labels, const float *lse, int64_t ntok,
+              int64_t V, const vl_range *rng, float scale, hipStream_t stream);
+
+/*
+ * Mean loss over the loss range, on the device [CE: read_loss, which sums
+ * the loss of every row and divides by the rows in the range].
+ *   loss  [ntok] float32, read only (may be NULL when ntok == 0).
+ *   mean  one float32 on the device, written: (sum of loss[0..ntok)) / (rows
+ *         in rng), or 0 when rng holds no row.  Summed in float64 in a fixed
+ *         order, so the result does not vary from run to run, and rounded
+ *         once to float32.
+ * Unlike the other calls, ntok == 0 still writes *mean (as 0).  The caller
+ * copies *mean back whenever it needs the value; nothing here synchronises.
+ */
+int vl_loss_mean(const float *loss, int64_t ntok, const vl_range *rng, float *mean,
+                 hipStream_t stream);
 
 /*
  * Fused distillation KL forward + backward [KL: module doc, kl_rows].

@@ -25,9 +25,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(vl_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_the_eight_calls():
     assert declared_functions() == sorted(
-        ["vl_ce_fwd_bwd", "vl_kl_fwd_bwd", "vl_topk_renorm", "vl_slice_acc", "vl_strerror"])
+        ["vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
+         "vl_topk_renorm", "vl_slice_acc", "vl_strerror"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -85,6 +86,34 @@ def test_ce_host_checks(lib):
     assert ce(lib, rng=rng(8, 0, 9)) == VL_EINVAL
     # ntok == 0 is a no-op, even with null pointers
     assert ce(lib, ntok=0, logits=None, labels=None, loss=None) == VL_OK
+
+
+def test_ce_split_host_checks(lib):
+    fwd, bwd = lib.vl_ce_fwd, lib.vl_ce_bwd
+    assert fwd(P, 2, P, P, None, 4, 10, None, None) == VL_EDTYPE
+    assert fwd(P, 0, P, P, None, 4, 0, None, None) == VL_EINVAL
+    assert fwd(P, 0, P, P, None, -1, 10, None, None) == VL_EINVAL
+    assert fwd(None, 0, P, P, None, 4, 10, None, None) == VL_EINVAL
+    assert fwd(P, 0, None, P, None, 4, 10, None, None) == VL_EINVAL
+    assert fwd(P, 0, P, None, None, 4, 10, None, None) == VL_EINVAL
+    assert fwd(P, 0, P, P, None, 4, 10, rng(4, 3, 2), None) == VL_EINVAL
+    assert fwd(None, 0, None, None, None, 0, 10, None, None) == VL_OK
+    assert bwd(P, 5, P, P, 4, 10, None, 1.0, None) == VL_EDTYPE
+    assert bwd(P, 0, P, P, 4, 1 << 31, None, 1.0, None) == VL_EINVAL
+    assert bwd(None, 0, P, P, 4, 10, None, 1.0, None) == VL_EINVAL
+    assert bwd(P, 0, None, P, 4, 10, None, 1.0, None) == VL_EINVAL
+    assert bwd(P, 0, P, None, 4, 10, None, 1.0, None) == VL_EINVAL  # lse is required
+    assert bwd(P, 0, P, P, 4, 10, rng(0, 0, 0), 1.0, None) == VL_EINVAL
+    assert bwd(None, 1, None, None, 0, 10, None, 1.0, None) == VL_OK
+
+
+def test_loss_mean_host_checks(lib):
+    f = lib.vl_loss_mean
+    assert f(P, -1, None, P, None) == VL_EINVAL
+    assert f(P, 4, None, None, None) == VL_EINVAL
+    assert f(None, 4, None, P, None) == VL_EINVAL
+    assert f(P, 4, rng(4, 2, 5), P, None) == VL_EINVAL
+    assert f(P, 4, rng(0, 0, 0), P, None) == VL_EINVAL
 
 
 def test_kl_host_checks(lib):

@@ -66,6 +66,39 @@ def test_ce_lm_full(vl):
         check_grad(x[r0:r1].cpu().numpy(), og, "f32", scale)
 
 
+def test_ce_split_lm_full(vl):
+    """The same configuration through the two-call CE (forward only, backward
+    from the saved lse) and the device mean: every row, and the mean against
+    the oracle's mean of the oracle's losses."""
+    c = gi.ce_lm(DEV)
+    x, lab, rng, scale = c["logits"], c["labels"], c["rng"], c["scale"]
+    host = to_host_bytes(x)
+    labh = lab.cpu().numpy()
+    n = x.shape[0]
+    loss = torch.empty(n, device=DEV)
+    lse = torch.empty(n, device=DEV)
+    mean = torch.empty(1, device=DEV)
+    vl.vl_ce_fwd(x, lab, loss, lse, rng=rng)
+    vl.vl_loss_mean(loss, mean, rng=rng)
+    vl.vl_ce_bwd(x, lab, lse, rng=rng, scale=scale)
+    torch.cuda.synchronize()
+    loss_h, lse_h = loss.cpu().numpy(), lse.cpu().numpy()
+    all_loss = np.empty(n)
+    for r0 in range(0, n, 512):
+        r1 = r0 + 512
+        ol, olse, og = oracle.ce(host[r0:r1], labh[r0:r1], rng=rng, scale=scale,
+                                 row_index=np.arange(r0, r1))
+        all_loss[r0:r1] = ol
+        check_loss(loss_h[r0:r1], ol, "f32")
+        check_loss(lse_h[r0:r1], olse, "f32", "lse")
+        check_grad(x[r0:r1].cpu().numpy(), og, "f32", scale)
+    # per-row losses within 1e-5 relative, so their mean is too
+    want = all_loss.sum() / (8 * 384)
+    assert abs(float(mean.cpu()[0]) - want) <= 1e-5 * abs(want)
+    assert abs(float(mean.cpu()[0]) - oracle.loss_mean(loss_h, rng)) <= np.spacing(
+        np.float32(want))
+
+
 def test_topk_zipf_full(vl):
     """Teacher top-k, 4096 x 32000, k=64: every row."""
     c = gi.topk_zipf(DEV)

@@ -22,7 +22,8 @@ import torch
 
 __all__ = [
     "VL_F32", "VL_BF16", "VLError", "lib_path",
-    "vl_ce_fwd_bwd", "vl_kl_fwd_bwd", "vl_topk_renorm", "vl_slice_acc", "vl_strerror",
+    "vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
+    "vl_topk_renorm", "vl_slice_acc", "vl_strerror",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -47,17 +48,21 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"{_LIB_PATH} is missing: build it with "
-            "`python -m vocab_softmax_loss_amd.build` (hipcc, gfx950)")
+            "`python vocab_softmax_loss_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     rp = ctypes.POINTER(vl_range)
     lib.vl_ce_fwd_bwd.argtypes = [vp, i32, vp, vp, vp, i64, i64, rp, f32, vp]
+    lib.vl_ce_fwd.argtypes = [vp, i32, vp, vp, vp, i64, i64, rp, vp]
+    lib.vl_ce_bwd.argtypes = [vp, i32, vp, vp, i64, i64, rp, f32, vp]
+    lib.vl_loss_mean.argtypes = [vp, i64, rp, vp, vp]
     lib.vl_kl_fwd_bwd.argtypes = [vp, i32, vp, vp, i64, vp, vp, i64, i64, rp, f32, vp]
     lib.vl_topk_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
     lib.vl_slice_acc.argtypes = [vp, vp, i64, vp]
     lib.vl_strerror.argtypes = [i32]
     lib.vl_strerror.restype = ctypes.c_char_p
-    for f in (lib.vl_ce_fwd_bwd, lib.vl_kl_fwd_bwd, lib.vl_topk_renorm, lib.vl_slice_acc):
+    for f in (lib.vl_ce_fwd_bwd, lib.vl_ce_fwd, lib.vl_ce_bwd, lib.vl_loss_mean,
+              lib.vl_kl_fwd_bwd, lib.vl_topk_renorm, lib.vl_slice_acc):
         f.restype = i32
     return lib
 
@@ -127,6 +132,38 @@ def vl_ce_fwd_bwd(logits, labels, loss, lse=None, rng=None, scale=1.0, stream=No
             _dev(loss, "loss", (torch.float32,), (ntok,)),
             None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
             ntok, V, _range(rng), float(scale), _stream(logits, stream)), "vl_ce_fwd_bwd")
+
+
+def vl_ce_fwd(logits, labels, loss, lse=None, rng=None, stream=None):
+    """CE forward only (logits read only); see vl_ce_fwd in vl.h."""
+    ntok, V = logits.shape
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_ce_fwd(
+            _dev(logits, "logits", None), _dtype_code(logits),
+            _dev(labels, "labels", _INT_IDS, (ntok,)),
+            _dev(loss, "loss", (torch.float32,), (ntok,)),
+            None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, V, _range(rng), _stream(logits, stream)), "vl_ce_fwd")
+
+
+def vl_ce_bwd(logits, labels, lse, rng=None, scale=1.0, stream=None):
+    """CE backward from a saved lse, written over the logits; see vl_ce_bwd."""
+    ntok, V = logits.shape
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_ce_bwd(
+            _dev(logits, "logits", None), _dtype_code(logits),
+            _dev(labels, "labels", _INT_IDS, (ntok,)),
+            _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, V, _range(rng), float(scale), _stream(logits, stream)), "vl_ce_bwd")
+
+
+def vl_loss_mean(loss, mean, rng=None, stream=None):
+    """mean[0] = loss.sum() / (rows in rng), on the device; see vl_loss_mean."""
+    ntok = loss.numel()
+    with torch.cuda.device(loss.device):
+        _check(_lib.vl_loss_mean(
+            _dev(loss, "loss", (torch.float32,), (ntok,)), ntok, _range(rng),
+            _dev(mean, "mean", (torch.float32,), (1,)), _stream(loss, stream)), "vl_loss_mean")
 
 
 def vl_kl_fwd_bwd(logits, ids, probs, loss, lse=None, rng=None, coef=1.0, stream=None):

@@ -1,6 +1,8 @@
 """Build libvl.so (the HIP kernels and the C ABI) for gfx950, in-tree.
 
-    python -m vocab_softmax_loss_amd.build
+    python vocab_softmax_loss_amd/build.py
+
+(run as a script, not as ``-m``: importing the package loads libvl.so.)
 
 Each source compiles to its own object under ``_build/`` (in parallel), then
 hipcc links them into ``vocab_softmax_loss_amd/libvl.so``.  Packed float32
@@ -22,7 +24,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvl.so")
 ARCH = os.environ.get("VL_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["vl_api.cpp", "vl_rows.hip", "vl_topk.hip", "vl_acc.hip"]
+SOURCES = ["vl_api.cpp", "vl_rows.hip", "vl_ce_split.hip", "vl_topk.hip", "vl_acc.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

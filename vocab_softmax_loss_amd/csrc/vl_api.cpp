@@ -29,6 +29,39 @@ int device_cus()
     return cus[dev];
 }
 
+namespace {
+
+struct OccKey {
+    const void *fn;
+    size_t lds;
+    int dev;
+};
+
+}  // namespace
+
+int blocks_per_cu(const void *fn, int block, size_t lds)
+{
+    static thread_local OccKey keys[64];
+    static thread_local int vals[64];
+    static thread_local int n = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    for (int i = 0; i < n; ++i)
+        if (keys[i].fn == fn && keys[i].lds == lds && keys[i].dev == dev)
+            return vals[i];
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, lds) != hipSuccess)
+        nb = 1;
+    if (nb < 1)
+        nb = 1;
+    if (n < 64) {
+        keys[n] = {fn, lds, dev};
+        vals[n] = nb;
+        ++n;
+    }
+    return nb;
+}
+
 }  // namespace vl
 
 namespace {
@@ -84,6 +117,56 @@ int vl_ce_fwd_bwd(void *logits, int dtype, const uint32_t *labels, float *loss, 
     a.k = 1;
     a.coef = scale;
     return status_of(vl::launch_rows(dtype, false, a, stream));
+}
+
+int vl_ce_fwd(const void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
+              int64_t ntok, int64_t V, const vl_range *rng, hipStream_t stream)
+{
+    vl::RowArgs a{};
+    int st = check_rows(dtype, ntok, V, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (ntok == 0)
+        return VL_OK;
+    if (!logits || !labels || !loss)
+        return VL_EINVAL;
+    // read only: the kernel never stores through it
+    a.logits = const_cast<void *>(logits);
+    a.labels = labels;
+    a.loss = loss;
+    a.lse = lse;
+    return status_of(vl::launch_ce_fwd(dtype, a, stream));
+}
+
+int vl_ce_bwd(void *logits, int dtype, const uint32_t *labels, const float *lse, int64_t ntok,
+              int64_t V, const vl_range *rng, float scale, hipStream_t stream)
+{
+    vl::RowArgs a{};
+    int st = check_rows(dtype, ntok, V, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (ntok == 0)
+        return VL_OK;
+    if (!logits || !labels || !lse)
+        return VL_EINVAL;
+    a.logits = logits;
+    a.labels = labels;
+    a.lse = const_cast<float *>(lse);  // read only in the backward
+    a.coef = scale;
+    return status_of(vl::launch_ce_bwd(dtype, a, stream));
+}
+
+int vl_loss_mean(const float *loss, int64_t ntok, const vl_range *rng, float *mean,
+                 hipStream_t stream)
+{
+    vl::RowArgs a{};
+    // the range checks of the loss calls (dtype and V play no part here)
+    int st = check_rows(VL_F32, ntok, 1, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (!mean || (ntok > 0 && !loss))
+        return VL_EINVAL;
+    return status_of(vl::launch_loss_mean(loss, ntok, a.walk.n_in, mean, stream));
 }
 
 int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *probs, int64_t k,

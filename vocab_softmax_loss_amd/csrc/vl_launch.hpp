@@ -102,9 +102,21 @@ struct TopkArgs {
 hipError_t launch_rows(int dtype, bool kl, const RowArgs &a, hipStream_t stream);
 hipError_t launch_topk(int dtype, const TopkArgs &a, hipStream_t stream);
 hipError_t launch_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream);
+// Cross-entropy in two calls, with RowArgs as for launch_rows: the forward
+// reads the logits and writes loss and lse (lse may be null); the backward
+// reads lse and writes the gradient over the logits (coef is the scale).
+hipError_t launch_ce_fwd(int dtype, const RowArgs &a, hipStream_t stream);
+hipError_t launch_ce_bwd(int dtype, const RowArgs &a, hipStream_t stream);
+// mean[0] = (sum of loss[0..n)) / count, or 0 when count is 0.
+hipError_t launch_loss_mean(const float *loss, int64_t n, int64_t count, float *mean,
+                            hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_cus();
+
+// Resident blocks per CU of kernel `fn` with `block` threads and `lds` bytes
+// of dynamic LDS on the current device (at least 1; cached).
+int blocks_per_cu(const void *fn, int block, size_t lds);
 
 // Largest KL vocabulary: two row bitmaps of V bits must fit in LDS.
 constexpr int64_t kMaxKlVocab = int64_t(1) << 19;

@@ -617,35 +617,6 @@ namespace {
 // the kernel's static arrays (under 1 KB).
 constexpr size_t kMaxDynLds = 160 * 1024 - 1024;
 
-struct OccKey {
-    const void *fn;
-    size_t lds;
-    int dev;
-};
-
-int cached_blocks_per_cu(const void *fn, int block, size_t lds)
-{
-    static thread_local OccKey keys[64];
-    static thread_local int vals[64];
-    static thread_local int n = 0;
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    for (int i = 0; i < n; ++i)
-        if (keys[i].fn == fn && keys[i].lds == lds && keys[i].dev == dev)
-            return vals[i];
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, lds) != hipSuccess)
-        nb = 1;
-    if (nb < 1)
-        nb = 1;
-    if (n < 64) {
-        keys[n] = {fn, lds, dev};
-        vals[n] = nb;
-        ++n;
-    }
-    return nb;
-}
-
 template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false, bool RL = false>
 hipError_t launch_one(const RowArgs &a, hipStream_t st)
 {
@@ -679,7 +650,7 @@ hipError_t launch_one(const RowArgs &a, hipStream_t st)
                 return e;
         }
     }
-    int per_cu = cached_blocks_per_cu((const void *)fn, BLOCK, lds);
+    int per_cu = blocks_per_cu((const void *)fn, BLOCK, lds);
     if (NV == 0 && per_cu > 1)
         per_cu = 1;  // online: keep the rows in flight inside the Infinity Cache
     const int64_t rows = a.walk.n_in > a.walk.n_out ? a.walk.n_in : a.walk.n_out;
