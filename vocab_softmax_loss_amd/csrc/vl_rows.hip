@@ -26,13 +26,13 @@
 //    right after its gradient is stored (RL).  float32 keeps
 //    e = exp(s - m_thread) in place of s and stores e * coef *
 //    exp(m_thread - lse): one exp per element.
-//  * online (NV == 0): the row is streamed twice: pass 1 keeps a running
-//    (max, sum) per thread with one rescale per chunk, pass 2 writes the
-//    gradient (2R + 1W).  The row's leading vectors, as many as the
-//    block's spare LDS holds, are kept there by pass 1 for pass 2; one
-//    1024-thread block per CU keeps the rows in flight small enough for
-//    the rest of the second pass to find much of them in the Infinity
-//    Cache.
+//  * online (NV == 0): pass 1 keeps a running (max, sum) per thread with
+//    one rescale per chunk, pass 2 writes the gradient.  Pass 1 leaves the
+//    row's first HK chunks in registers (float32: half of a 128256-value
+//    row) and the next vectors, as many as the block's spare LDS holds, in
+//    LDS, so pass 2 reads only the rest again; one 1024-thread block per
+//    CU keeps the rows in flight small enough for part of that re-read to
+//    come from the Infinity Cache.
 // (max, sum) pairs reduce across the wave with DPP and across waves through
 // LDS, one barrier per row (an LDS-only barrier: it does not wait for the
 // prefetched loads); the LDS slots alternate by row parity so a fast wave
@@ -62,9 +62,9 @@ namespace vl {
 
 // Vectors per thread per chunk of the online variant.
 template <int N>
-constexpr int online_unroll()
+constexpr int online_unroll(int hk = 0)
 {
-    return N == 1 ? 16 : 8;
+    return N == 1 ? 16 : (hk > 0 ? 4 : 8);
 }
 
 // PF (staged only): stream the next row into an LDS buffer with asynchronous
@@ -72,14 +72,19 @@ constexpr int online_unroll()
 // and stored.  Each lane reads back only the 16-byte slots its own loads
 // wrote, so the buffer needs no barrier, only this wave's own waits.
 // Without PF the occupancy of several blocks per CU provides the overlap.
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL>
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL, int HK>
 struct RowKernel {
     using IO = RowIO<DT, VEC>;
     using Raw = typename IO::Raw;
     static constexpr int N = IO::N;
     static constexpr int NW = BLOCK / kWave;
-    static constexpr int U = online_unroll<N>();
+    static constexpr int U = online_unroll<N>(NV > 0 ? 0 : HK);
     static constexpr int NB = NV > 0 ? NV : 1;
+    // Online: the row's first NH chunks of BLOCK x U vectors stay in
+    // registers from pass 1 to pass 2; LDS keeps the nlds vectors after them.
+    static constexpr int NH = NV > 0 ? 0 : HK;
+    static constexpr uint32_t kChunk = (uint32_t)BLOCK * U;
+    static constexpr uint32_t kHeld = (uint32_t)NH * kChunk;
     // float32 vectors hold 4 values in 4 registers, so the staged buffer can
     // take exp(s - m) in place of s; bf16 holds 8 values in 4 registers.
     static constexpr bool kKeepExp = (DT == kF32) && VEC && NV > 0;
@@ -140,7 +145,7 @@ struct RowKernel {
     __device__ uint32_t fresh_tid() const
     {
         uint32_t t = (uint32_t)tid;
-        if constexpr (RL)
+        if constexpr (RL || NH > 0)
             __asm__ __volatile__("" : "+v"(t));
         return t;
     }
@@ -256,6 +261,53 @@ struct RowKernel {
         }
     }
 
+    // Online pass 1: fold one chunk of U vectors (v0 + u BLOCK) into the
+    // thread's running (max, sum) with a single rescale.
+    __device__ void online_chunk(const Raw (&y)[U], uint32_t v0, float &m, float &s) const
+    {
+        float cm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[N];
+            unpack_masked(y[u], v0 + (uint32_t)u * BLOCK, x);
+#pragma unroll
+            for (int c = 0; c < N; ++c)
+                cm = fmaxf(cm, x[c]);
+        }
+        const float mn = fmaxf(m, cm);
+        if (mn != -INFINITY) {
+            float acc = s * __expf(m - mn);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float x[N];
+                unpack_masked(y[u], v0 + (uint32_t)u * BLOCK, x);
+#pragma unroll
+                for (int c = 0; c < N; ++c)
+                    acc += __expf(x[c] - mn);
+            }
+            s = acc;
+            m = mn;
+        }
+    }
+
+    // Online pass 2: the gradient of one chunk and its stores.
+    __device__ void store_chunk(char *p, const Raw (&y)[U], uint32_t v0, float lse, const Tgt &t,
+                                const uint32_t *bm) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t v = v0 + (uint32_t)u * BLOCK;
+            if (v < nvec) {
+                float x[N], g[N];
+                IO::unpack(y[u], x);
+#pragma unroll
+                for (int c = 0; c < N; ++c)
+                    g[c] = coef * __expf(x[c] - lse);
+                store_vec(p, v, g, t, bm);
+            }
+        }
+    }
+
     // One in-range row: reduce, loss, gradient.  `buf` holds the row when
     // staged; with RL each register is refilled with the next row's vector
     // as soon as its own gradient is stored.  Afterwards the next row's
@@ -267,6 +319,7 @@ struct RowKernel {
         uint32_t *bm = bitmaps + par * words;
         uint32_t *bm_other = bitmaps + (par ^ 1) * words;
         const uint32_t t0 = fresh_tid();
+        Raw hold[NH > 0 ? NH : 1][U];  // online: the row's first NH chunks
 
         // ---- pass 1: thread-local (max, sum of exp)
         float m = -INFINITY, s = 0.f;
@@ -301,7 +354,18 @@ struct RowKernel {
                 vector_fence();
             }
         } else {
-            for (uint32_t v0 = tid; v0 < nvec; v0 += (uint32_t)BLOCK * U) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const uint32_t v0 = t0 + (uint32_t)h * kChunk;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    hold[h][u] = IO::load_raw(p, clamp_vec(v0 + (uint32_t)u * BLOCK));
+                online_chunk(hold[h], v0, m, s);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    __asm__ __volatile__("" : "+v"(hold[h][u]) : "v"(s));
+            }
+            for (uint32_t v0 = t0 + kHeld; v0 < nvec; v0 += kChunk) {
                 Raw y[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u)
@@ -309,31 +373,9 @@ struct RowKernel {
                 // nlds is a multiple of BLOCK: each test is uniform
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    if (v0 + (uint32_t)u * BLOCK < nlds)
-                        lrow[v0 + (uint32_t)u * BLOCK] = y[u];
-                float cm = -INFINITY;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float x[N];
-                    unpack_masked(y[u], v0 + (uint32_t)u * BLOCK, x);
-#pragma unroll
-                    for (int c = 0; c < N; ++c)
-                        cm = fmaxf(cm, x[c]);
-                }
-                const float mn = fmaxf(m, cm);
-                if (mn != -INFINITY) {
-                    float acc = s * __expf(m - mn);
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        float x[N];
-                        unpack_masked(y[u], v0 + (uint32_t)u * BLOCK, x);
-#pragma unroll
-                        for (int c = 0; c < N; ++c)
-                            acc += __expf(x[c] - mn);
-                    }
-                    s = acc;
-                    m = mn;
-                }
+                    if (v0 - kHeld + (uint32_t)u * BLOCK < nlds)
+                        lrow[v0 - kHeld + (uint32_t)u * BLOCK] = y[u];
+                online_chunk(y, v0, m, s);
             }
         }
 
@@ -458,25 +500,22 @@ struct RowKernel {
                 vector_fence();
             }
         } else {
-            for (uint32_t v0 = tid; v0 < nvec; v0 += (uint32_t)BLOCK * U) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                // widened again here, not kept widened from pass 1
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    __asm__ __volatile__("" : "+v"(hold[h][u]) : "v"(lse));
+                store_chunk(p, hold[h], fresh_tid() + (uint32_t)h * kChunk, lse, t, bm);
+            }
+            for (uint32_t v0 = fresh_tid() + kHeld; v0 < nvec; v0 += kChunk) {
                 Raw y[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const uint32_t v = v0 + (uint32_t)u * BLOCK;
-                    y[u] = v < nlds ? lrow[v] : IO::load_raw(p, clamp_vec(v));
+                    y[u] = v - kHeld < nlds ? lrow[v - kHeld] : IO::load_raw(p, clamp_vec(v));
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t v = v0 + (uint32_t)u * BLOCK;
-                    if (v < nvec) {
-                        float x[N], g[N];
-                        IO::unpack(y[u], x);
-#pragma unroll
-                        for (int c = 0; c < N; ++c)
-                            g[c] = coef * __expf(x[c] - lse);
-                        store_vec(p, v, g, t, bm);
-                    }
-                }
+                store_chunk(p, y, v0, lse, t, bm);
             }
         }
 
@@ -593,7 +632,7 @@ constexpr int min_waves_per_simd()
     return 1;
 }
 
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL>
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL, int HK>
 __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void row_loss_kernel(
     RowArgs a)
 {
@@ -603,7 +642,7 @@ __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void 
     __shared__ float sh_l[2][NW];
     // Dynamic LDS: [PF: BLOCK x NV 16-byte slots][KL: 2 x ceil(V/32) words]
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
-    using K = RowKernel<DT, KL, BLOCK, NV, VEC, PF, RL>;
+    using K = RowKernel<DT, KL, BLOCK, NV, VEC, PF, RL, HK>;
     constexpr uint32_t pf_words = PF ? (uint32_t)BLOCK * (NV > 0 ? NV : 1) * 4 : 0;
     K k(a, sh_m, sh_s, sh_l, dyn + pf_words, reinterpret_cast<typename K::Raw *>(dyn));
     k.run();
@@ -617,10 +656,11 @@ namespace {
 // the kernel's static arrays (under 1 KB).
 constexpr size_t kMaxDynLds = 160 * 1024 - 1024;
 
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false, bool RL = false>
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false, bool RL = false,
+          int HK = 0>
 hipError_t launch_one(const RowArgs &a, hipStream_t st)
 {
-    auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF, RL>;
+    auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF, RL, HK>;
     RowArgs args = a;
     size_t lds = 0;
     if (PF)
@@ -629,14 +669,16 @@ hipError_t launch_one(const RowArgs &a, hipStream_t st)
         lds += ((2 * (size_t)((a.V + 31) >> 5) + 3) & ~size_t(3)) * sizeof(uint32_t);
     args.lds_vecs = 0;
     if (NV == 0) {
-        // Online: the rest of LDS keeps the row's leading vectors, in units
-        // of BLOCK, for pass 2, which reads them from there instead of HBM.
-        // Those are the first read in pass 1, the least likely to be still
-        // cached.
+        // Online: after the HK chunks held in registers, the rest of LDS
+        // keeps the row's next vectors, in units of BLOCK, for pass 2, which
+        // reads them from there instead of HBM.  Those are the first read in
+        // pass 1, the least likely to be still cached.
         const size_t unit = (size_t)BLOCK * sizeof(typename RowIO<DT, VEC>::Raw);
         const size_t room = lds < kMaxDynLds ? (kMaxDynLds - lds) / unit : 0;
         const int64_t nvec = a.V / RowIO<DT, VEC>::N;
-        const int64_t units = (nvec + BLOCK - 1) / BLOCK;
+        const int64_t held = (int64_t)HK * BLOCK * online_unroll<RowIO<DT, VEC>::N>(HK);
+        const int64_t rest = nvec > held ? nvec - held : 0;
+        const int64_t units = (rest + BLOCK - 1) / BLOCK;
         const int64_t keep = (int64_t)room < units ? (int64_t)room : units;
         args.lds_vecs = keep * BLOCK;
         lds += (size_t)keep * unit;
@@ -699,7 +741,13 @@ hipError_t launch_dt(const RowArgs &a, hipStream_t st, bool vec)
         if (nvec <= 1024 * 19)
             return launch_one<DT, KL, 1024, 19, true, false, true>(a, st);
     }
-    return launch_one<DT, KL, 1024, 0, true>(a, st);
+    // Rows past the registers, online: float32 holds the row's first four
+    // chunks (64 registers a thread) in registers, the next part in LDS, and
+    // streams the rest twice.
+    if constexpr (DT == kF32)
+        return launch_one<DT, KL, 1024, 0, true, false, false, 4>(a, st);
+    else
+        return launch_one<DT, KL, 1024, 0, true>(a, st);
 }
 
 }  // namespace
