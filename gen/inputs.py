@@ -220,6 +220,43 @@ def page_ce_tiny():
     return dict(logits=logits, labels=labels, rng=(4, 0, 4), scale=0.25)
 
 
+def page_head_tiny():
+    """cortiq-engine ``train_head.rs`` test ``head_kl_matches_host``: V=1024,
+    hs=256, 45 tokens, k=16; head weights ``rnd(V*hs, 1, 0.1)`` and hidden
+    rows ``rnd(45*hs, 2, 1.0)`` as float32 (each side rounds them to f16
+    itself), teacher ids (t*37 + q*61) mod V with probabilities the
+    normalised exponential of ``rnd(k, 100 + t, 1.0)``; gscale 256, total
+    45, chunks of 32 rows."""
+    V, hs, ntok, k = 1024, 256, 45, 16
+    w = page_rnd(V * hs, 1, 0.1).reshape(V, hs)
+    x = page_rnd(ntok * hs, 2, 1.0).reshape(ntok, hs)
+    ids = np.empty((ntok, k), dtype=np.int32)
+    probs = np.empty((ntok, k), dtype=np.float32)
+    for t in range(ntok):
+        raw = page_rnd(k, 100 + t, 1.0)
+        e = np.exp(raw.astype(np.float32))
+        z = np.float32(0.0)
+        for q in range(k):
+            z = np.float32(z + e[q])
+        for q in range(k):
+            ids[t, q] = (t * 37 + q * 61) % V
+            probs[t, q] = e[q] / z
+    return dict(x=x, w=w, ids=ids, probs=probs, total=ntok, gscale=256.0, chunk=32)
+
+
+def head_inputs(ntok: int, V: int, hs: int, k: int, seed: int, device, wdtype=torch.bfloat16):
+    """Vocabulary head inputs: hidden rows x ~ N(0, 1) float32 [ntok][hs];
+    head weights ~ N(0, 1/hs) [V][hs] rounded once to ``wdtype`` (the head is
+    frozen and stored in half precision); k distinct uniform teacher ids per
+    row with probabilities softmax(N(0, 1.5^2)) (float64, cast to float32)."""
+    g = _gen(seed, device)
+    x = torch.randn((ntok, hs), generator=g, device=device)
+    w = (torch.randn((V, hs), generator=g, device=device) * (1.0 / hs) ** 0.5).to(wdtype)
+    ids = distinct_ids(ntok, V, k, seed + 1, device)
+    probs = softmax_probs(ntok, k, 1.5, seed + 2, device)
+    return dict(x=x, w=w, ids=ids, probs=probs)
+
+
 def page_kl_tiny():
     """cortiq-engine ``train_head.rs`` test ``head_kl_matches_host`` inputs,
     with the logits handed over directly: V=1024, hs=256, 45 tokens, k=16.

@@ -1,9 +1,10 @@
 """Float64 CPU oracle of the fused vocabulary-softmax loss (ctypes loader).
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
-benchmark's CPU-baseline leg; never by the product path.  The arithmetic is
-in ``oracle.c``; this module only builds that file with gcc, loads it and
-marshals numpy arrays.
+benchmark's CPU-baseline leg; never by the product path.  The row
+arithmetic is in ``oracle.c``; this module builds that file with gcc, loads
+it and marshals numpy arrays.  The vocabulary head (``head_kl``) is numpy
+float64 here: two library matrix products around the KL rows.
 
 Logits are numpy arrays ``[n][V]``: float32, or uint16 holding bf16 bit
 patterns.  Labels and ids are read as uint32.
@@ -170,3 +171,55 @@ def acc(dst, src):
     out = np.empty_like(d)
     _load().oracle_acc(_ptr(d), _ptr(s), d.size, _ptr(out))
     return out.reshape(np.shape(dst))
+
+
+# ---------------------------------------------------------------- head
+
+def round_half(x, dtype):
+    """float32 values rounded to nearest even in "f16" or "bf16", returned
+    as float64.  The hidden rows and the head weights are rounded once
+    this way before both products."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return f.astype(np.float16).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def head_kl(x, w, ids, probs, total, gscale):
+    """Vocabulary head with the distillation KL (cortiq-engine
+    train_head.rs, head_kl), float64, on hidden rows ``x`` [n][hs] and head
+    ``w`` [V][hs] given as float64 values (already rounded the way the GPU
+    rounds them, see ``round_half``):
+
+      s_t = w x_t                                  (logits, a library matmul)
+      loss_t = sum over q with p_q > 0 of p_q (ln p_q - (s_t[id_q] - lse_t))
+      d_t = (gscale / total) (softmax(s_t) - t_t)  (the KL rows' in-place gradient)
+      dx_t = d_t w / gscale                        (the input gradient)
+
+    so dx is the gradient of sum_t loss_t / total with the teacher term
+    applied as given.  Returns (loss [n], dx [n][hs]), float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    n = x.shape[0]
+    idv = np.ascontiguousarray(ids).astype(np.int64).reshape(n, -1)
+    pv = np.ascontiguousarray(probs, dtype=np.float32).astype(np.float64).reshape(n, -1)
+    s = x @ w.T
+    m = s.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+    loss = np.zeros(n)
+    coef = float(gscale) / float(total)
+    d = np.exp(s - lse[:, None])
+    for t in range(n):
+        for q in range(idv.shape[1]):
+            pq = pv[t, q]
+            if pq > 0.0:
+                loss[t] += pq * (np.log(pq) - (s[t, idv[t, q]] - lse[t]))
+            d[t, idv[t, q]] -= pq
+    d *= coef
+    dx = (d @ w) / float(gscale)
+    return loss, dx

@@ -513,3 +513,72 @@ def test_acc_bit_exact_float32_add():
     with np.errstate(over="ignore"):
         want = a + b  # numpy float32 add: correctly rounded, an independent route
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ----------------------------------------------------------------- head
+
+def head_case(n=4, V=48, hs=12, k=5, seed=3):
+    r = np.random.default_rng(seed)
+    x = r.normal(size=(n, hs))
+    w = r.normal(size=(V, hs)) * 0.4
+    ids = np.stack([r.choice(V, size=k, replace=False) for _ in range(n)])
+    z = r.normal(size=(n, k)) * 1.5
+    p = np.exp(z) / np.exp(z).sum(axis=1, keepdims=True)
+    return x, w, ids, p
+
+
+def test_head_dx_is_the_gradient_of_the_mean_loss():
+    """Central differences of sum_t loss_t / total in each hidden entry
+    match dx (the teacher probabilities sum to 1 up to float32 rounding, so
+    the literal p_S - p_T gradient is the derivative)."""
+    x, w, ids, p = head_case()
+    total, gscale = 7, 256.0
+    _, dx = oracle.head_kl(x, w, ids, p, total, gscale)
+    h = 1e-6
+    for t in range(x.shape[0]):
+        for i in range(x.shape[1]):
+            xp = x.copy(); xp[t, i] += h
+            xm = x.copy(); xm[t, i] -= h
+            lp, _ = oracle.head_kl(xp, w, ids, p, total, gscale)
+            lm, _ = oracle.head_kl(xm, w, ids, p, total, gscale)
+            fd = (lp.sum() - lm.sum()) / (2 * h * total)
+            assert abs(fd - dx[t, i]) < 1e-6 * max(1.0, abs(dx[t, i])), (t, i, fd, dx[t, i])
+
+
+def test_head_zero_weights_closed_form():
+    """W = 0: every logit is 0, the student is uniform: loss = sum_q p_q
+    ln(p_q V), and dx = 0."""
+    x, w, ids, p = head_case()
+    V = w.shape[0]
+    loss, dx = oracle.head_kl(x, np.zeros_like(w), ids, p, 4, 2.0)
+    pf = p.astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(loss, (pf * np.log(pf * V)).sum(axis=1), rtol=1e-13)
+    assert not dx.any()
+
+
+def test_head_matches_the_row_kl_on_exact_logits():
+    """With dyadic inputs whose products are exact in float32, the head's
+    loss equals the C oracle's KL on those logits and dx equals that
+    gradient times W over gscale: the two are written separately."""
+    r = np.random.default_rng(9)
+    n, V, hs, k = 5, 64, 8, 6
+    x = r.integers(-4, 5, size=(n, hs)) / 4.0
+    w = r.integers(-8, 9, size=(V, hs)) / 8.0
+    ids = np.stack([r.choice(V, size=k, replace=False) for _ in range(n)])
+    p = (r.dirichlet(np.ones(k), size=n)).astype(np.float32)
+    s = (x @ w.T).astype(np.float32)
+    assert np.array_equal(s.astype(np.float64), x @ w.T)
+    total, gscale = 9, 64.0
+    loss, dx = oracle.head_kl(x, w, ids, p, total, gscale)
+    kloss, _, g = oracle.kl(s, ids.astype(np.uint32), p, coef=gscale / total)
+    np.testing.assert_allclose(loss, kloss, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(dx, (g @ w) / gscale, rtol=1e-12, atol=1e-15)
+
+
+def test_round_half_is_round_to_nearest_even():
+    """f16 by numpy's cast; bf16 ties go to the even pattern."""
+    one = np.float32(1.0)
+    tie = np.array([1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, -(1.0 + 2.0**-8)], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.round_half(tie, "bf16"), [1.0, 1.0 + 2**-6, -1.0])
+    assert oracle.round_half(np.float32(1.0 + 2.0**-11), "f16") == 1.0
+    assert oracle.round_half(one, "bf16") == 1.0
