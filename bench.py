@@ -18,7 +18,8 @@ Prints one JSON line.  `value` is logits rows per second of the whole step;
 the launch stream around every launch of the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-                    [--workload step|ce_lm|ce_split|topk_zipf|kl_large|kl_bf16|copy_calib]
+                    [--workload step|ce_lm|ce_split|topk_zipf|kl_large|kl_bf16|head_kl|
+                                copy_calib]
     python bench.py --pmc-summary <counter_collection.csv> ...
 
 The other workloads time one configuration each at its full size, for
@@ -187,6 +188,21 @@ def other_workload(name, dev):
                   "acc": 3 * ntok * hs * 4}
         cfg = {"workload": gi.KL_BF16.name, "ntok": ntok, "V": V, "k": k, "dtype": "bf16",
                "bytes_model": "KL 1R+1W"}
+    elif name == "head_kl":
+        # the vocabulary head around the KL: two GEMMs of 2 ntok V hs flops
+        # each on the matrix cores, the KL rows and two conversions between
+        c = gi.head_inputs(16384, 151936, 1024, 256, 6001, dev, torch.bfloat16)
+        ntok, hs = c["x"].shape
+        V, k, chunk, gscale = c["w"].shape[0], c["ids"].shape[1], 4096, 1024.0
+        dx = torch.empty((ntok, hs), device=dev)
+        loss = torch.empty(ntok, device=dev)
+        scratch = torch.empty(vl.vl_head_scratch_bytes(chunk, V, hs), dtype=torch.uint8,
+                              device=dev)
+        calls = [("head", lambda: vl.vl_head_kl(c["x"], c["w"], c["ids"], c["probs"], dx, loss,
+                                                ntok, gscale, chunk, scratch))]
+        nbytes = {"head": None}
+        cfg = {"workload": "head_16384x151936x1024_bf16_k256", "ntok": ntok, "V": V, "hs": hs,
+               "k": k, "chunk": chunk, "dtype": "bf16", "flops": 2 * 2 * ntok * V * hs}
     elif name == "copy_calib":
         n = COPY_CALIB_BYTES // 4
         src = torch.randn(n, device=dev)
@@ -266,9 +282,15 @@ def time_calls(calls, steps, warmup):
     return per, t0.elapsed_time(t1) / steps
 
 
+MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/f16 matrix peak
+
+
 def kernel_table(per_ms, nbytes, ntok):
     out = {}
     for n, ms in per_ms.items():
+        if nbytes[n] is None:
+            out[n] = {"ms": round(ms, 5), "rows/s": round(ntok / (ms * 1e-3), 1)}
+            continue
         gbs = nbytes[n] / (ms * 1e-3) / 1e9
         out[n] = {"ms": round(ms, 5), "bytes": nbytes[n], "GB/s": round(gbs, 1),
                   "frac": round(gbs / HBM_PEAK_GBS, 4), "rows/s": round(ntok / (ms * 1e-3), 1)}
@@ -303,16 +325,23 @@ def main():
         per, seq_ms = time_calls(calls, args.steps, args.warmup)
         kernels = kernel_table(per, nbytes, ntok)
         dom = max(per, key=per.get)
+        if "flops" in cfg:
+            # matrix-core bound: the whole call's flops over its time
+            tf = cfg["flops"] / (per[dom] * 1e-3) / 1e12
+            roof = {"kernel": dom, "bound": "mfma", "achieved": round(tf, 1),
+                    "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None}
+        else:
+            roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB/s"],
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
+                    "traffic": None}
         print(json.dumps({
             "metric": f"rows/s and achieved HBM GB/s of one configuration ({args.workload})",
             "value": round(ntok / (seq_ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(seq_ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": cfg["dtype"], "data": "synthetic", "config": cfg,
-            "roofline": {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB/s"],
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
-                         "traffic": None},
-            "kernels": kernels, "cpu_baseline": None}), flush=True)
+            "roofline": roof, "kernels": kernels, "cpu_baseline": None}), flush=True)
         return
     x = make_inputs(dev)
     host = None if args.no_cpu else host_copies(x)

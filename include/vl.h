@@ -13,11 +13,13 @@
  *        (distillation KL against the teacher's renormalised top-k and its
  *        gradient p_S - p_T, written in place and scaled), kl_rows, topk_rows
  *        (teacher top-k with probabilities renormalised over the k), acc_add
- *        (one vocabulary slice's input gradient added into another's).
+ *        (one vocabulary slice's input gradient added into another's),
+ *        head_kl (the head's two products around the KL rows).
  *
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller.  The library keeps
- *     no reference after the call returns and allocates no memory.
+ *     no reference after the call returns and allocates no memory (except
+ *     vl_head_kl's hipBLASLt handle, below).
  *   - Calls are asynchronous on `stream` (0 = the null stream of the current
  *     device); the caller observes completion on that stream.
  *   - Matrices are row-major and contiguous: row r of logits starts at
@@ -47,8 +49,9 @@ extern "C" {
 #endif
 
 /* Element type of logits: IEEE float32, or bfloat16 (widened exactly to
- * float32; stores round to nearest even). */
-typedef enum { VL_F32 = 0, VL_BF16 = 1 } vl_dtype;
+ * float32; stores round to nearest even).  VL_F16 (IEEE half) is accepted
+ * only as the head's weight type (vl_head_kl). */
+typedef enum { VL_F32 = 0, VL_BF16 = 1, VL_F16 = 2 } vl_dtype;
 
 /* Loss range [CE: CEForwardParams / read_loss].  Row r takes part in the
  * loss iff start <= r % seq_len < end; with seq_len == ntok this is one
@@ -165,6 +168,42 @@ int vl_topk_renorm(const void *logits, int dtype, int64_t ntok, int64_t V, int64
  *   dst [n] float32, read and written;  src [n] float32, read only.
  */
 int vl_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream);
+
+/*
+ * Scratch bytes vl_head_kl needs for `chunk` rows at a time: float32 logits
+ * [chunk][V], the half-precision hidden rows [chunk][hs] and gradient
+ * [chunk][V], and a 64 MiB GEMM workspace, each 256-byte aligned.
+ */
+size_t vl_head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
+
+/*
+ * Vocabulary head with the distillation KL [KL: head_kl, Head, HeadScratch]:
+ * for chunks of `chunk` rows,
+ *   act    = half(x rows)                        (round to nearest even)
+ *   logits = act . w^T                           (float32 accumulation)
+ *   KL rows as vl_kl_fwd_bwd with coef = gscale / total, giving loss and the
+ *           gradient coef (softmax - t) over the logits
+ *   dx     = half(gradient) . w / gscale          (float32 accumulation)
+ * so dx is the gradient of (sum of the rows' KL) / total with respect to x,
+ * the teacher term applied as given.
+ *   x       [ntok][hs] float32, read only: the normed hidden rows.
+ *   w       [V][hs] head weights in wdtype (VL_F16 or VL_BF16), read only.
+ *   ids, probs, k   as for vl_kl_fwd_bwd.
+ *   dx      [ntok][hs] float32, written.
+ *   loss    [ntok] float32, written: the KL of each row, unscaled.
+ *   total   the tokens the step averages over (>= 1); gscale != 0, finite.
+ *   scratch device buffer of at least vl_head_scratch_bytes(min(chunk,
+ *           ntok), V, hs) bytes, owned by the caller; its contents on entry
+ *           do not matter and are undefined after the call.
+ * The two products run in hipBLASLt; its handle is created on the first
+ * call on each device and kept until the process ends (the only allocation
+ * the library makes).  Limits: 1 <= k <= V <= 2^19, hs >= 1, chunk >= 1.
+ * Returns VL_ELAUNCH if hipBLASLt finds no algorithm or rejects a call.
+ */
+int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
+               const float *probs, int64_t k, float *dx, float *loss, int64_t ntok, int64_t V,
+               int64_t hs, int64_t total, float gscale, int64_t chunk, void *scratch,
+               size_t scratch_bytes, hipStream_t stream);
 
 /* Static text naming a status code. */
 const char *vl_strerror(int status);

@@ -25,10 +25,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(vl_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_eight_calls():
+def test_header_declares_the_ten_calls():
     assert declared_functions() == sorted(
         ["vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
-         "vl_topk_renorm", "vl_slice_acc", "vl_strerror"])
+         "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
+         "vl_strerror"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -149,3 +150,42 @@ def test_slice_acc_host_checks(lib):
     assert f(None, P, 4, None) == VL_EINVAL
     assert f(P, None, 4, None) == VL_EINVAL
     assert f(None, None, 0, None) == VL_OK
+
+
+def test_head_scratch_bytes(lib):
+    f = lib.vl_head_scratch_bytes
+    a = 256
+    up = lambda b: (b + a - 1) // a * a  # noqa: E731
+    want = up(32 * 1024 * 4) + up(32 * 256 * 2) + up(32 * 1024 * 2) + (64 << 20)
+    assert f(32, 1024, 256) == want
+    assert f(0, 1024, 256) == 0 and f(32, 0, 256) == 0 and f(32, 1024, 0) == 0
+    assert f(32, (1 << 19) + 1, 256) == 0
+
+
+def test_head_host_checks(lib):
+    f = lib.vl_head_kl
+    ok = dict(x=P, w=P, wd=1, ids=P, probs=P, k=4, dx=P, loss=P, ntok=8, V=64, hs=16,
+              total=8, gscale=1.0, chunk=4, scratch=P, sb=1 << 40, st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["w"], a["wd"], a["ids"], a["probs"], a["k"], a["dx"], a["loss"],
+                 a["ntok"], a["V"], a["hs"], a["total"], a["gscale"], a["chunk"], a["scratch"],
+                 a["sb"], a["st"])
+    assert call(wd=0) == VL_EDTYPE  # float32 weights are not a head type
+    assert call(wd=3) == VL_EDTYPE
+    assert call(k=0) == VL_EINVAL
+    assert call(k=65) == VL_EINVAL
+    assert call(V=(1 << 19) + 1) == VL_EINVAL
+    assert call(hs=0) == VL_EINVAL
+    assert call(total=0) == VL_EINVAL
+    assert call(chunk=0) == VL_EINVAL
+    assert call(gscale=0.0) == VL_EINVAL
+    assert call(gscale=float("inf")) == VL_EINVAL
+    assert call(gscale=float("nan")) == VL_EINVAL
+    assert call(ntok=-1) == VL_EINVAL
+    assert call(sb=1000) == VL_EINVAL  # scratch too small
+    for name in ("x", "w", "ids", "probs", "dx", "loss", "scratch"):
+        assert call(**{name: None}) == VL_EINVAL, name
+    assert call(ntok=0, x=None, scratch=None) == VL_OK

@@ -172,3 +172,31 @@ def test_kl_bf16_sliced_full(vl):
     vl.vl_slice_acc(d0, d1)
     torch.cuda.synchronize()
     assert np.array_equal(d0.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_head_kl_full(vl):
+    """Vocabulary head, 16384 x 151936 x 1024 bf16, k=256, chunks of 4096 (the
+    bench configuration): sampled rows, chunk edges included, against the
+    oracle on those rows (each row's loss and dx depend on that row alone).
+    Tolerances as in tests/test_gpu_head.py."""
+    c = gi.head_inputs(16384, 151936, 1024, 256, 6001, DEV, torch.bfloat16)
+    x, w, ids, probs = c["x"], c["w"], c["ids"], c["probs"]
+    ntok, hs = x.shape
+    V = w.shape[0]
+    dx = torch.empty((ntok, hs), device=DEV)
+    loss = torch.empty(ntok, device=DEV)
+    scratch = torch.empty(vl.vl_head_scratch_bytes(4096, V, hs), dtype=torch.uint8, device=DEV)
+    vl.vl_head_kl(x, w, ids, probs, dx, loss, ntok, 1024.0, 4096, scratch)
+    torch.cuda.synchronize()
+    rows = sample(ntok, 12, 61, extra=(0, 4095, 4096, 8191, 12288, ntok - 1))
+    xr = oracle.round_half(x[rows].cpu().numpy(), "bf16")
+    wr = w.float().cpu().numpy().astype(np.float64)
+    rl, rdx = oracle.head_kl(xr, wr, ids[rows].cpu().numpy(), probs[rows].cpu().numpy(), ntok,
+                             1024.0)
+    got_l = loss.cpu().numpy()[rows].astype(np.float64)
+    got_dx = dx.cpu().numpy()[rows].astype(np.float64)
+    assert np.isfinite(loss.cpu().numpy()).all() and bool(torch.isfinite(dx).all())
+    assert (np.abs(got_l - rl) <= 1e-4 + 1e-5 * np.abs(rl)).all(), (got_l, rl)
+    for i in range(len(rows)):
+        e = np.linalg.norm(got_dx[i] - rdx[i]) / np.linalg.norm(rdx[i])
+        assert e < 2.4e-2, (rows[i], e)

@@ -21,9 +21,9 @@ import os
 import torch
 
 __all__ = [
-    "VL_F32", "VL_BF16", "VLError", "lib_path",
+    "VL_F32", "VL_BF16", "VL_F16", "VLError", "lib_path",
     "vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
-    "vl_topk_renorm", "vl_slice_acc", "vl_strerror",
+    "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl", "vl_strerror",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +31,7 @@ _LIB_PATH = os.path.join(_PKG, "libvl.so")
 
 VL_F32 = 0
 VL_BF16 = 1
+VL_F16 = 2
 
 
 class VLError(RuntimeError):
@@ -59,6 +60,11 @@ def _load():
     lib.vl_kl_fwd_bwd.argtypes = [vp, i32, vp, vp, i64, vp, vp, i64, i64, rp, f32, vp]
     lib.vl_topk_renorm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
     lib.vl_slice_acc.argtypes = [vp, vp, i64, vp]
+    lib.vl_head_scratch_bytes.argtypes = [i64, i64, i64]
+    lib.vl_head_scratch_bytes.restype = ctypes.c_size_t
+    lib.vl_head_kl.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, i64, i64, i64, i64, f32, i64,
+                               vp, ctypes.c_size_t, vp]
+    lib.vl_head_kl.restype = i32
     lib.vl_strerror.argtypes = [i32]
     lib.vl_strerror.restype = ctypes.c_char_p
     for f in (lib.vl_ce_fwd_bwd, lib.vl_ce_fwd, lib.vl_ce_bwd, lib.vl_loss_mean,
@@ -199,3 +205,31 @@ def vl_slice_acc(dst, src, stream=None):
             _dev(dst, "dst", (torch.float32,)),
             _dev(src, "src", (torch.float32,), tuple(dst.shape)), n,
             _stream(dst, stream)), "vl_slice_acc")
+
+
+def vl_head_scratch_bytes(chunk, V, hs):
+    """Bytes of scratch vl_head_kl needs for `chunk` rows at a time."""
+    return int(_lib.vl_head_scratch_bytes(int(chunk), int(V), int(hs)))
+
+
+def vl_head_kl(x, w, ids, probs, dx, loss, total, gscale, chunk, scratch, stream=None):
+    """Vocabulary head + distillation KL; see vl_head_kl in vl.h.  ``w`` is
+    a torch.float16 or torch.bfloat16 [V][hs] tensor; ``scratch`` a uint8
+    device tensor of at least vl_head_scratch_bytes(min(chunk, ntok), V, hs)
+    bytes."""
+    ntok, hs = x.shape
+    V = w.shape[0]
+    k = ids.shape[1] if ids.dim() == 2 else 0
+    wd = {torch.float16: VL_F16, torch.bfloat16: VL_BF16}.get(w.dtype)
+    if wd is None:
+        raise TypeError(f"w must be float16 or bfloat16, got {w.dtype}")
+    with torch.cuda.device(x.device):
+        _check(_lib.vl_head_kl(
+            _dev(x, "x", (torch.float32,)), _dev(w, "w", None, (V, hs)), wd,
+            _dev(ids, "ids", _INT_IDS, (ntok, k)),
+            _dev(probs, "probs", (torch.float32,), (ntok, k)), k,
+            _dev(dx, "dx", (torch.float32,), (ntok, hs)),
+            _dev(loss, "loss", (torch.float32,), (ntok,)),
+            ntok, V, hs, int(total), float(gscale), int(chunk),
+            _dev(scratch, "scratch", (torch.uint8,)), scratch.numel(),
+            _stream(x, stream)), "vl_head_kl")

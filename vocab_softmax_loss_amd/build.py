@@ -24,7 +24,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvl.so")
 ARCH = os.environ.get("VL_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["vl_api.cpp", "vl_rows.hip", "vl_ce_split.hip", "vl_topk.hip", "vl_acc.hip"]
+SOURCES = ["vl_api.cpp", "vl_rows.hip", "vl_ce_split.hip", "vl_topk.hip", "vl_acc.hip",
+           "vl_head.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -61,7 +62,8 @@ def build(jobs: int | None = None) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+           "-L/opt/rocm/lib", "-lhipblaslt"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

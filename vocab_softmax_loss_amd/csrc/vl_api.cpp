@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
+
 #include <mutex>
 
 #include "vl_launch.hpp"
@@ -169,6 +171,37 @@ int vl_loss_mean(const float *loss, int64_t ntok, const vl_range *rng, float *me
     return status_of(vl::launch_loss_mean(loss, ntok, a.walk.n_in, mean, stream));
 }
 
+size_t vl_head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
+{
+    if (chunk < 1 || V < 1 || hs < 1 || V > vl::kMaxKlVocab || hs > kMaxV)
+        return 0;
+    return vl::head_scratch_bytes(chunk, V, hs);
+}
+
+int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
+               const float *probs, int64_t k, float *dx, float *loss, int64_t ntok, int64_t V,
+               int64_t hs, int64_t total, float gscale, int64_t chunk, void *scratch,
+               size_t scratch_bytes, hipStream_t stream)
+{
+    if (wdtype != VL_BF16 && wdtype != VL_F16)
+        return VL_EDTYPE;
+    if (ntok < 0 || V < 1 || V > vl::kMaxKlVocab || hs < 1 || hs > kMaxV || k < 1 || k > V ||
+        total < 1 || chunk < 1 || !(gscale != 0.f) || !isfinite(gscale))
+        return VL_EINVAL;
+    if (ntok > INT64_MAX / (V > hs ? V : hs) || ntok > INT64_MAX / k)
+        return VL_EINVAL;
+    if (ntok == 0)
+        return VL_OK;
+    if (!x || !w || !ids || !probs || !dx || !loss || !scratch)
+        return VL_EINVAL;
+    const int64_t c = chunk < ntok ? chunk : ntok;
+    if (scratch_bytes < vl::head_scratch_bytes(c, V, hs))
+        return VL_EINVAL;
+    vl::HeadArgs a{x, w, wdtype, ids, probs, dx, loss, ntok, V, hs, k, total, c, gscale,
+                   scratch};
+    return vl::head_kl(a, stream);
+}
+
 int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *probs, int64_t k,
                   float *loss, float *lse, int64_t ntok, int64_t V, const vl_range *rng,
                   float coef, hipStream_t stream)
@@ -234,7 +267,7 @@ const char *vl_strerror(int status)
     case VL_EDTYPE:
         return "unknown dtype (expected VL_F32 or VL_BF16)";
     case VL_ELAUNCH:
-        return "the HIP runtime rejected the kernel launch";
+        return "the HIP runtime rejected a kernel launch, or hipBLASLt a product";
     default:
         return "unknown status";
     }

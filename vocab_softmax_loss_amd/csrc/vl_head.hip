@@ -1,0 +1,221 @@
+// Vocabulary head with the distillation KL for gfx950 (cortiq-engine
+// train_head.rs: Head, HeadScratch, head_kl).  For each chunk of rows:
+//   act    = half(x[r0:r1])                         [rows][hs]   (to_half_kernel)
+//   logits = act . W^T, float32 accumulate          [rows][V]    (hipBLASLt, "TN")
+//   KL rows against the teacher, coef = gscale / total: loss, and the
+//   gradient written over the logits                             (row_loss_kernel)
+//   dl     = half(gradient)                         [rows][V]    (to_half_kernel)
+//   dx[r0:r1] = dl . W / gscale, float32 accumulate [rows][hs]   (hipBLASLt, "NN")
+// "half" is the head's type, f16 or bf16, rounded to nearest even.  The two
+// products are plain GEMMs on the matrix cores and go to hipBLASLt; the row
+// work between them is this library's own kernels.  The page slices the
+// head into vocabulary planes because a WebGPU storage binding stops at
+// 2 GiB; HIP has no such limit, so each product spans the whole vocabulary.
+#include <hipblaslt/hipblaslt.h>
+#include <math.h>
+
+#include <mutex>
+
+#include "vl.h"
+#include "vl_device.hpp"
+#include "vl_launch.hpp"
+
+namespace vl {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// dst[i] = half(src[i]) for i < n; 8 per thread from 16-byte aligned
+// float32 (VEC), one at a time otherwise.  src is read once: non-temporal.
+template <bool BF, bool VEC>
+__global__ __launch_bounds__(256) void to_half_kernel(const float *src, void *dst, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t done = 0;
+    if constexpr (VEC) {
+        const int64_t n8 = n / 8;
+        const f32x4 *s4 = reinterpret_cast<const f32x4 *>(src);
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+            const f32x4 a = __builtin_nontemporal_load(s4 + 2 * i);
+            const f32x4 b = __builtin_nontemporal_load(s4 + 2 * i + 1);
+            const f32x8 f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            if constexpr (BF)
+                reinterpret_cast<bf16x8 *>(dst)[i] = __builtin_convertvector(f, bf16x8);
+            else
+                reinterpret_cast<f16x8 *>(dst)[i] = __builtin_convertvector(f, f16x8);
+        }
+        done = n8 * 8;
+    }
+    for (int64_t i = done + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        if constexpr (BF)
+            reinterpret_cast<__bf16 *>(dst)[i] = (__bf16)src[i];
+        else
+            reinterpret_cast<_Float16 *>(dst)[i] = (_Float16)src[i];
+    }
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kHeadWorkspace = size_t(64) << 20;  // hipBLASLt workspace
+
+size_t align_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
+
+struct HeadLayout {
+    size_t logits, act, dl, ws, total;
+};
+
+HeadLayout head_layout(int64_t chunk, int64_t V, int64_t hs)
+{
+    HeadLayout L{};
+    L.logits = 0;
+    L.act = align_up((size_t)chunk * (size_t)V * 4);
+    L.dl = L.act + align_up((size_t)chunk * (size_t)hs * 2);
+    L.ws = L.dl + align_up((size_t)chunk * (size_t)V * 2);
+    L.total = L.ws + kHeadWorkspace;
+    return L;
+}
+
+hipError_t to_half(bool bf, const float *src, void *dst, int64_t n, hipStream_t st)
+{
+    const bool vec = (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0;
+    const int64_t per = vec ? 8 : 1;
+    int64_t grid = (n / per + 255) / 256;
+    const int64_t cap = (int64_t)device_cus() * 8;
+    if (grid > cap)
+        grid = cap;
+    if (grid < 1)
+        grid = 1;
+    if (bf) {
+        if (vec)
+            hipLaunchKernelGGL((to_half_kernel<true, true>), dim3((unsigned)grid), dim3(256), 0, st,
+                               src, dst, n);
+        else
+            hipLaunchKernelGGL((to_half_kernel<true, false>), dim3((unsigned)grid), dim3(256), 0,
+                               st, src, dst, n);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((to_half_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0,
+                               st, src, dst, n);
+        else
+            hipLaunchKernelGGL((to_half_kernel<false, false>), dim3((unsigned)grid), dim3(256), 0,
+                               st, src, dst, n);
+    }
+    return hipGetLastError();
+}
+
+// One hipBLASLt handle per device, created on first use and kept.
+hipblasLtHandle_t lt_handle()
+{
+    static std::mutex mu;
+    static hipblasLtHandle_t handles[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!handles[dev] && hipblasLtCreate(&handles[dev]) != HIPBLAS_STATUS_SUCCESS)
+        handles[dev] = nullptr;
+    return handles[dev];
+}
+
+// Column-major C (m x n, ldc, float32) = alpha op(A) op(B), A and B half
+// precision of type `ht`, float32 accumulation.  op(A) is m x k, op(B) k x n.
+bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int64_t m,
+          int64_t n, int64_t k, float alpha, const void *A, int64_t lda, const void *B,
+          int64_t ldb, float *C, int64_t ldc, hipDataType ht, void *ws, size_t ws_bytes,
+          hipStream_t st)
+{
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    bool ok = hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) ==
+              HIPBLAS_STATUS_SUCCESS;
+    const int32_t opa = ta, opb = tb;
+    ok = ok && hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opa,
+                                               sizeof opa) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opb,
+                                               sizeof opb) == HIPBLAS_STATUS_SUCCESS;
+    // stored shapes (before op)
+    const uint64_t ar = ta == HIPBLAS_OP_N ? m : k, ac = ta == HIPBLAS_OP_N ? k : m;
+    const uint64_t br = tb == HIPBLAS_OP_N ? k : n, bc = tb == HIPBLAS_OP_N ? n : k;
+    ok = ok && hipblasLtMatrixLayoutCreate(&la, ht, ar, ac, lda) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&lb, ht, br, bc, ldb) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&lc, HIP_R_32F, m, n, ldc) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
+    const uint64_t wsb = ws_bytes;
+    ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref,
+                                                     HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                     &wsb, sizeof wsb) == HIPBLAS_STATUS_SUCCESS;
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int found = 0;
+    ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, 1, res, &found) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    ok = ok && found > 0 && res[0].workspaceSize <= ws_bytes;
+    const float beta = 0.f;
+    ok = ok && hipblasLtMatmul(h, desc, &alpha, A, la, B, lb, &beta, C, lc, C, lc, &res[0].algo,
+                               ws, ws_bytes, st) == HIPBLAS_STATUS_SUCCESS;
+    if (pref)
+        hipblasLtMatmulPreferenceDestroy(pref);
+    if (lc)
+        hipblasLtMatrixLayoutDestroy(lc);
+    if (lb)
+        hipblasLtMatrixLayoutDestroy(lb);
+    if (la)
+        hipblasLtMatrixLayoutDestroy(la);
+    if (desc)
+        hipblasLtMatmulDescDestroy(desc);
+    return ok;
+}
+
+}  // namespace
+
+size_t head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
+{
+    return head_layout(chunk, V, hs).total;
+}
+
+int head_kl(const HeadArgs &a, hipStream_t st)
+{
+    hipblasLtHandle_t h = lt_handle();
+    if (!h)
+        return VL_ELAUNCH;
+    const bool bf = a.wdtype == VL_BF16;
+    const hipDataType ht = bf ? HIP_R_16BF : HIP_R_16F;
+    const int64_t chunk = a.chunk < a.ntok ? a.chunk : a.ntok;
+    const HeadLayout L = head_layout(chunk, a.V, a.hs);
+    char *base = static_cast<char *>(a.scratch);
+    float *logits = reinterpret_cast<float *>(base + L.logits);
+    void *act = base + L.act;
+    void *dl = base + L.dl;
+    void *ws = base + L.ws;
+    const float coef = a.gscale / (float)a.total;
+    for (int64_t r0 = 0; r0 < a.ntok; r0 += chunk) {
+        const int64_t rows = a.ntok - r0 < chunk ? a.ntok - r0 : chunk;
+        if (to_half(bf, a.x + r0 * a.hs, act, rows * a.hs, st) != hipSuccess)
+            return VL_ELAUNCH;
+        // logits (row-major rows x V) = column-major V x rows = W . act^T
+        if (!gemm(h, HIPBLAS_OP_T, HIPBLAS_OP_N, a.V, rows, a.hs, 1.f, a.w, a.hs, act, a.hs,
+                  logits, a.V, ht, ws, kHeadWorkspace, st))
+            return VL_ELAUNCH;
+        RowArgs r{};
+        r.logits = logits;
+        r.ids = a.ids + r0 * a.k;
+        r.probs = a.probs + r0 * a.k;
+        r.loss = a.loss + r0;
+        r.ntok = rows;
+        r.V = a.V;
+        r.k = a.k;
+        r.walk = make_walk(rows, 0, 0, 0);
+        r.coef = coef;
+        if (launch_rows(kF32, true, r, st) != hipSuccess)
+            return VL_ELAUNCH;
+        if (to_half(bf, logits, dl, rows * a.V, st) != hipSuccess)
+            return VL_ELAUNCH;
+        // dx (row-major rows x hs) = column-major hs x rows = W^T . dl^T
+        if (!gemm(h, HIPBLAS_OP_N, HIPBLAS_OP_N, a.hs, rows, a.V, 1.f / a.gscale, a.w, a.hs, dl,
+                  a.V, a.dx + r0 * a.hs, a.hs, ht, ws, kHeadWorkspace, st))
+            return VL_ELAUNCH;
+    }
+    return VL_OK;
+}
+
+}  // namespace vl

@@ -98,6 +98,25 @@ struct TopkArgs {
     float *probs;        // [ntok][k]
 };
 
+// One call of the vocabulary head with the KL (checked by the caller).
+struct HeadArgs {
+    const float *x;         // [ntok][hs] hidden rows
+    const void *w;          // [V][hs] head weights, wdtype
+    int wdtype;             // VL_F16 or VL_BF16
+    const uint32_t *ids;    // [ntok][k]
+    const float *probs;     // [ntok][k]
+    float *dx;              // [ntok][hs]
+    float *loss;            // [ntok]
+    int64_t ntok, V, hs, k, total, chunk;
+    float gscale;
+    void *scratch;          // head_scratch_bytes(min(chunk, ntok), V, hs) bytes
+};
+
+// Scratch bytes of one head call with `chunk` rows at a time.
+size_t head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
+// Returns a VL_ status.
+int head_kl(const HeadArgs &a, hipStream_t stream);
+
 // Each returns hipSuccess or the HIP error of the launch.
 hipError_t launch_rows(int dtype, bool kl, const RowArgs &a, hipStream_t stream);
 hipError_t launch_topk(int dtype, const TopkArgs &a, hipStream_t stream);
