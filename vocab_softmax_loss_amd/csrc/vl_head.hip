@@ -3,8 +3,7 @@
 //   act    = half(x[r0:r1])                         [rows][hs]   (to_half_kernel)
 //   logits = act . W^T, float32 accumulate          [rows][V]    (hipBLASLt, "TN")
 //   KL rows against the teacher, coef = gscale / total: loss, and the
-//   gradient written over the logits                             (row_loss_kernel)
-//   dl     = half(gradient)                         [rows][V]    (to_half_kernel)
+//   gradient rounded to half as it is stored: dl    [rows][V]    (row_loss_kernel)
 //   dx[r0:r1] = dl . W / gscale, float32 accumulate [rows][hs]   (hipBLASLt, "NN")
 // "half" is the head's type, f16 or bf16, rounded to nearest even.  The two
 // products are plain GEMMs on the matrix cores and go to hipBLASLt; the row
@@ -15,6 +14,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <vector>
 
 #include "vl.h"
 #include "vl_device.hpp"
@@ -117,6 +117,60 @@ hipblasLtHandle_t lt_handle()
     return handles[dev];
 }
 
+// The algorithm each GEMM shape runs with, per device.  hipBLASLt's first
+// heuristic choice is not its fastest for these shapes (the logits product
+// at 4096 x 151936 x 1024 bf16: 1.73 ms against 1.35 ms for the best of its
+// first 16), so the first call with a shape times the candidates once, on
+// the caller's stream, and later calls reuse the fastest.  Under stream
+// capture nothing is timed and the first choice runs.
+struct AlgoKey {
+    int dev, ta, tb, ht;
+    int64_t m, n, k;
+    bool operator==(const AlgoKey &o) const
+    {
+        return dev == o.dev && ta == o.ta && tb == o.tb && ht == o.ht && m == o.m && n == o.n &&
+               k == o.k;
+    }
+};
+
+struct AlgoEntry {
+    AlgoKey key;
+    hipblasLtMatmulAlgo_t algo;
+};
+
+std::mutex algo_mu;
+std::vector<AlgoEntry> algo_cache;
+
+bool cached_algo(const AlgoKey &key, hipblasLtMatmulAlgo_t *out)
+{
+    std::lock_guard<std::mutex> lock(algo_mu);
+    for (const AlgoEntry &e : algo_cache)
+        if (e.key == key) {
+            *out = e.algo;
+            return true;
+        }
+    return false;
+}
+
+constexpr int kTuneCandidates = 16;
+
+bool finish(bool ok, hipblasLtMatmulDesc_t desc, hipblasLtMatrixLayout_t la,
+            hipblasLtMatrixLayout_t lb, hipblasLtMatrixLayout_t lc,
+            hipblasLtMatmulPreference_t pref)
+{
+    if (pref)
+        hipblasLtMatmulPreferenceDestroy(pref);
+    if (lc)
+        hipblasLtMatrixLayoutDestroy(lc);
+    if (lb)
+        hipblasLtMatrixLayoutDestroy(lb);
+    if (la)
+        hipblasLtMatrixLayoutDestroy(la);
+    if (desc)
+        hipblasLtMatmulDescDestroy(desc);
+    return ok;
+}
+
 // Column-major C (m x n, ldc, float32) = alpha op(A) op(B), A and B half
 // precision of type `ht`, float32 accumulation.  op(A) is m x k, op(B) k x n.
 bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int64_t m,
@@ -145,25 +199,59 @@ bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int
     ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref,
                                                      HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
                                                      &wsb, sizeof wsb) == HIPBLAS_STATUS_SUCCESS;
-    hipblasLtMatmulHeuristicResult_t res[1];
-    int found = 0;
-    ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, 1, res, &found) ==
-                   HIPBLAS_STATUS_SUCCESS;
-    ok = ok && found > 0 && res[0].workspaceSize <= ws_bytes;
     const float beta = 0.f;
-    ok = ok && hipblasLtMatmul(h, desc, &alpha, A, la, B, lb, &beta, C, lc, C, lc, &res[0].algo,
-                               ws, ws_bytes, st) == HIPBLAS_STATUS_SUCCESS;
-    if (pref)
-        hipblasLtMatmulPreferenceDestroy(pref);
-    if (lc)
-        hipblasLtMatrixLayoutDestroy(lc);
-    if (lb)
-        hipblasLtMatrixLayoutDestroy(lb);
-    if (la)
-        hipblasLtMatrixLayoutDestroy(la);
-    if (desc)
-        hipblasLtMatmulDescDestroy(desc);
-    return ok;
+    auto run = [&](const hipblasLtMatmulAlgo_t &algo) {
+        return hipblasLtMatmul(h, desc, &alpha, A, la, B, lb, &beta, C, lc, C, lc, &algo, ws,
+                               ws_bytes, st) == HIPBLAS_STATUS_SUCCESS;
+    };
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const AlgoKey key{dev, (int)ta, (int)tb, (int)ht, m, n, k};
+    hipblasLtMatmulAlgo_t algo{};
+    if (ok && cached_algo(key, &algo))
+        return finish(ok && run(algo), desc, la, lb, lc, pref);
+    hipblasLtMatmulHeuristicResult_t res[kTuneCandidates];
+    int found = 0;
+    ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, kTuneCandidates,
+                                               res, &found) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && found > 0 && res[0].workspaceSize <= ws_bytes;
+    if (!ok)
+        return finish(false, desc, la, lb, lc, pref);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone ||
+        found == 1)
+        return finish(run(res[0].algo), desc, la, lb, lc, pref);
+    // Time each candidate: one untimed run, then two timed ones.
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    int best = -1;
+    float best_ms = 0.f;
+    if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+        for (int i = 0; i < found; ++i) {
+            if (res[i].workspaceSize > ws_bytes || !run(res[i].algo))
+                continue;
+            float ms = 0.f;
+            if (hipEventRecord(e0, st) != hipSuccess || !run(res[i].algo) || !run(res[i].algo) ||
+                hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+                continue;
+            if (best < 0 || ms < best_ms) {
+                best = i;
+                best_ms = ms;
+            }
+        }
+    }
+    if (e0)
+        hipEventDestroy(e0);
+    if (e1)
+        hipEventDestroy(e1);
+    if (best < 0)
+        best = 0;
+    {
+        std::lock_guard<std::mutex> lock(algo_mu);
+        algo_cache.push_back({key, res[best].algo});
+    }
+    ok = run(res[best].algo);
+    return finish(ok, desc, la, lb, lc, pref);
 }
 
 }  // namespace
@@ -206,9 +294,8 @@ int head_kl(const HeadArgs &a, hipStream_t st)
         r.k = a.k;
         r.walk = make_walk(rows, 0, 0, 0);
         r.coef = coef;
-        if (launch_rows(kF32, true, r, st) != hipSuccess)
-            return VL_ELAUNCH;
-        if (to_half(bf, logits, dl, rows * a.V, st) != hipSuccess)
+        r.gout = dl;  // the gradient goes straight to the GEMM operand, rounded
+        if (launch_rows(kF32, true, r, st, bf ? 1 : 2) != hipSuccess)
             return VL_ELAUNCH;
         // dx (row-major rows x hs) = column-major hs x rows = W^T . dl^T
         if (!gemm(h, HIPBLAS_OP_N, HIPBLAS_OP_N, a.hs, rows, a.V, 1.f / a.gscale, a.w, a.hs, dl,

@@ -89,6 +89,7 @@ struct RowArgs {
     RowWalk walk;             // loss range as a row order
     float coef;               // gradient scale
     int64_t lds_vecs;         // online: leading vectors of a row kept in LDS for pass 2
+    void *gout;               // out != 0: [ntok][V] half-precision gradient rows
 };
 
 struct TopkArgs {
@@ -118,7 +119,9 @@ size_t head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
 int head_kl(const HeadArgs &a, hipStream_t stream);
 
 // Each returns hipSuccess or the HIP error of the launch.
-hipError_t launch_rows(int dtype, bool kl, const RowArgs &a, hipStream_t stream);
+// out = 0: the gradient is written over the logits; out = 1 / 2: float32 KL
+// rows write it rounded to bf16 / f16 into a.gout and leave the logits.
+hipError_t launch_rows(int dtype, bool kl, const RowArgs &a, hipStream_t stream, int out = 0);
 hipError_t launch_topk(int dtype, const TopkArgs &a, hipStream_t stream);
 hipError_t launch_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream);
 // Cross-entropy in two calls, with RowArgs as for launch_rows: the forward

@@ -72,7 +72,40 @@ constexpr int online_unroll(int hk = 0)
 // and stored.  Each lane reads back only the 16-byte slots its own loads
 // wrote, so the buffer needs no barrier, only this wave's own waits.
 // Without PF the occupancy of several blocks per CU provides the overlap.
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL, int HK>
+// Where the gradient goes: over the logits (OUT = 0), or, rounded to bf16
+// (OUT = 1) or f16 (OUT = 2), into a separate row-major [ntok][V] buffer
+// that the next step reads as a GEMM operand.
+template <bool BF, int N>
+__device__ __forceinline__ void half_store(char *q, uint32_t vi, const float (&g)[N])
+{
+    if constexpr (N == 4) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        const f32x4 f = {g[0], g[1], g[2], g[3]};
+        unsigned long long bits;
+        if constexpr (BF)
+            bits = __builtin_bit_cast(unsigned long long, __builtin_convertvector(f, bf16x4));
+        else
+            bits = __builtin_bit_cast(unsigned long long, __builtin_convertvector(f, f16x4));
+        __builtin_nontemporal_store(bits, reinterpret_cast<unsigned long long *>(q) + vi);
+    } else if constexpr (N == 8) {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        const f32x8 f = {g[0], g[1], g[2], g[3], g[4], g[5], g[6], g[7]};
+        u32x4 bits;
+        if constexpr (BF)
+            bits = __builtin_bit_cast(u32x4, __builtin_convertvector(f, bf16x8));
+        else
+            bits = __builtin_bit_cast(u32x4, __builtin_convertvector(f, f16x8));
+        __builtin_nontemporal_store(bits, reinterpret_cast<u32x4 *>(q) + vi);
+    } else {
+        if constexpr (BF)
+            reinterpret_cast<__bf16 *>(q)[vi] = (__bf16)g[0];
+        else
+            reinterpret_cast<_Float16 *>(q)[vi] = (_Float16)g[0];
+    }
+}
+
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL, int HK, int OUT>
 struct RowKernel {
     using IO = RowIO<DT, VEC>;
     using Raw = typename IO::Raw;
@@ -127,6 +160,33 @@ struct RowKernel {
     }
 
     __device__ uint32_t clamp_vec(uint32_t v) const { return v < nvec ? v : nvec - 1; }
+
+    // The gradient row of `row` (the logits row itself unless OUT) and its
+    // element size.
+    static constexpr uint32_t kOutElt = (OUT == 0 && DT == kF32) ? 4u : 2u;
+    __device__ char *grow(int64_t row) const
+    {
+        if constexpr (OUT == 0)
+            return rowp(row);
+        else
+            return reinterpret_cast<char *>(a.gout) + row * (int64_t)V * 2;
+    }
+    __device__ static void put(char *q, uint32_t vi, const float (&g)[N])
+    {
+        if constexpr (OUT == 0)
+            IO::store(q, vi, g);
+        else
+            half_store<OUT == 1, N>(q, vi, g);
+    }
+    __device__ static void put_elem(char *q, uint32_t j, float g)
+    {
+        if constexpr (OUT == 0)
+            IO::store_elem(q, j, g);
+        else if constexpr (OUT == 1)
+            reinterpret_cast<__bf16 *>(q)[j] = (__bf16)g;
+        else
+            reinterpret_cast<_Float16 *>(q)[j] = (_Float16)g;
+    }
 
     // Staged rows (NV > 0, always 16-byte vectors) are far below 4 GiB, so
     // vector v is at a 32-bit byte offset from the row base: one offset
@@ -236,27 +296,28 @@ struct RowKernel {
         }
     }
 
-    // The gradient of one vector, target handling included, and its store.
+    // The gradient of one vector, target handling included, and its store
+    // into gradient row `p`.
     __device__ void store_vec(char *p, uint32_t v, float (&g)[N], const Tgt &t,
                               const uint32_t *bm) const
     {
         // Staged rows: vector v at a 32-bit byte offset (see load_small).
-        char *q = NV > 0 ? p + v * (uint32_t)(N * elt_bytes<DT>()) : p;
+        char *q = NV > 0 ? p + v * (uint32_t)(N * kOutElt) : p;
         const uint32_t vi = NV > 0 ? 0u : v;  // vector index from q
         if constexpr (!KL) {
             if (t.label < V && v == t.label / N)
                 g[t.label % N] -= coef;
-            IO::store(q, vi, g);
+            put(q, vi, g);
         } else {
             const uint32_t j0 = v * N;
             const uint32_t bits = (bm[j0 >> 5] >> (j0 & 31)) & (uint32_t)((1ull << N) - 1);
             if (bits == 0u) {
-                IO::store(q, vi, g);
+                put(q, vi, g);
             } else if (__builtin_popcount(bits) > 1) {  // one target: its thread writes it all
 #pragma unroll
                 for (int c = 0; c < N; ++c)
                     if (!((bits >> c) & 1u))
-                        IO::store_elem(q, vi * N + c, g[c]);
+                        put_elem(q, vi * N + c, g[c]);
             }
         }
     }
@@ -316,6 +377,7 @@ struct RowKernel {
                             int64_t nrow, Tgt &tn) const
     {
         char *p = rowp(row);
+        char *gw = grow(row);
         uint32_t *bm = bitmaps + par * words;
         uint32_t *bm_other = bitmaps + (par ^ 1) * words;
         const uint32_t t0 = fresh_tid();
@@ -448,11 +510,11 @@ struct RowKernel {
 #pragma unroll
                         for (int c = 0; c < N; ++c)
                             g[c] = (uint32_t)c == id - j0 ? gid : coef * __expf(x[c] - lse);
-                        IO::store(p, v, g);
+                        put(gw, v, g);
                         continue;
                     }
                 }
-                IO::store_elem(p, id, gid);
+                put_elem(gw, id, gid);
             }
             const float wl = wave_sum(acc);
             if (lane == 0)
@@ -487,7 +549,7 @@ struct RowKernel {
 #pragma unroll
                     for (int c = 0; c < N; ++c)
                         g[c] = kKeepExp ? x[c] * cf : coef * __expf(x[c] - lse);
-                    store_vec(p, v, g, t, bm);
+                    store_vec(gw, v, g, t, bm);
                 }
                 if constexpr (RL) {
                     // Not before this vector's store: the register is the
@@ -506,7 +568,7 @@ struct RowKernel {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     __asm__ __volatile__("" : "+v"(hold[h][u]) : "v"(lse));
-                store_chunk(p, hold[h], fresh_tid() + (uint32_t)h * kChunk, lse, t, bm);
+                store_chunk(gw, hold[h], fresh_tid() + (uint32_t)h * kChunk, lse, t, bm);
             }
             for (uint32_t v0 = fresh_tid() + kHeld; v0 < nvec; v0 += kChunk) {
                 Raw y[U];
@@ -515,7 +577,7 @@ struct RowKernel {
                     const uint32_t v = v0 + (uint32_t)u * BLOCK;
                     y[u] = v - kHeld < nlds ? lrow[v - kHeld] : IO::load_raw(p, clamp_vec(v));
                 }
-                store_chunk(p, y, v0, lse, t, bm);
+                store_chunk(gw, y, v0, lse, t, bm);
             }
         }
 
@@ -527,13 +589,13 @@ struct RowKernel {
 
     __device__ void zero_row(int64_t row) const
     {
-        char *p = rowp(row);
+        char *p = grow(row);
         float z[N];
 #pragma unroll
         for (int c = 0; c < N; ++c)
             z[c] = 0.f;
         for (uint32_t v = tid; v < nvec; v += BLOCK)
-            IO::store(p, v, z);
+            put(p, v, z);
         if (tid == 0) {
             a.loss[row] = 0.f;
             if (a.lse)
@@ -632,7 +694,7 @@ constexpr int min_waves_per_simd()
     return 1;
 }
 
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL, int HK>
+template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL, int HK, int OUT>
 __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void row_loss_kernel(
     RowArgs a)
 {
@@ -642,7 +704,7 @@ __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void 
     __shared__ float sh_l[2][NW];
     // Dynamic LDS: [PF: BLOCK x NV 16-byte slots][KL: 2 x ceil(V/32) words]
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
-    using K = RowKernel<DT, KL, BLOCK, NV, VEC, PF, RL, HK>;
+    using K = RowKernel<DT, KL, BLOCK, NV, VEC, PF, RL, HK, OUT>;
     constexpr uint32_t pf_words = PF ? (uint32_t)BLOCK * (NV > 0 ? NV : 1) * 4 : 0;
     K k(a, sh_m, sh_s, sh_l, dyn + pf_words, reinterpret_cast<typename K::Raw *>(dyn));
     k.run();
@@ -656,11 +718,11 @@ namespace {
 // the kernel's static arrays (under 1 KB).
 constexpr size_t kMaxDynLds = 160 * 1024 - 1024;
 
-template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false, bool RL = false,
-          int HK = 0>
+template <int OUT, int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false,
+          bool RL = false, int HK = 0>
 hipError_t launch_one(const RowArgs &a, hipStream_t st)
 {
-    auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF, RL, HK>;
+    auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF, RL, HK, OUT>;
     RowArgs args = a;
     size_t lds = 0;
     if (PF)
@@ -704,62 +766,70 @@ hipError_t launch_one(const RowArgs &a, hipStream_t st)
 }
 
 // Staged variants: BLOCK threads x NV vectors cover the row.
-template <int DT, bool KL>
+template <int DT, bool KL, int OUT>
 hipError_t launch_dt(const RowArgs &a, hipStream_t st, bool vec)
 {
     constexpr int N = RowIO<DT, true>::N;
     if (!vec)
-        return launch_one<DT, KL, 256, 0, false>(a, st);
+        return launch_one<OUT, DT, KL, 256, 0, false>(a, st);
     const int64_t nvec = a.V / N;
     if (nvec <= 64)
-        return launch_one<DT, KL, 64, 1, true>(a, st);
+        return launch_one<OUT, DT, KL, 64, 1, true>(a, st);
     if (nvec <= 128)
-        return launch_one<DT, KL, 64, 2, true>(a, st);
+        return launch_one<OUT, DT, KL, 64, 2, true>(a, st);
     if (nvec <= 256)
-        return launch_one<DT, KL, 64, 4, true>(a, st);
+        return launch_one<OUT, DT, KL, 64, 4, true>(a, st);
     if constexpr (DT == kF32) {
         if (nvec <= 512)
-            return launch_one<DT, KL, 64, 8, true>(a, st);
+            return launch_one<OUT, DT, KL, 64, 8, true>(a, st);
         if (nvec <= 1024)
-            return launch_one<DT, KL, 256, 4, true>(a, st);
+            return launch_one<OUT, DT, KL, 256, 4, true>(a, st);
         if (nvec <= 2048)
-            return launch_one<DT, KL, 256, 8, true>(a, st);
+            return launch_one<OUT, DT, KL, 256, 8, true>(a, st);
         // One 512-thread block per CU, the next row streaming into LDS.
         if (nvec <= 4096)
-            return launch_one<DT, KL, 512, 8, true, true>(a, st);
+            return launch_one<OUT, DT, KL, 512, 8, true, true>(a, st);
         if (nvec <= 8192)
-            return launch_one<DT, KL, 512, 16, true, true>(a, st);
+            return launch_one<OUT, DT, KL, 512, 16, true, true>(a, st);
     } else {
         // bf16 widens to twice its register footprint: at most 8 vectors
         // (64 values) per thread.
         if (nvec <= 1024)
-            return launch_one<DT, KL, 256, 4, true>(a, st);
+            return launch_one<OUT, DT, KL, 256, 4, true>(a, st);
         if (nvec <= 4096)
-            return launch_one<DT, KL, 512, 8, true, true>(a, st);
+            return launch_one<OUT, DT, KL, 512, 8, true, true>(a, st);
         // One 1024-thread block per CU holds the whole row in registers and
         // refills them with the next row as the gradient is stored.
         if (nvec <= 1024 * 19)
-            return launch_one<DT, KL, 1024, 19, true, false, true>(a, st);
+            return launch_one<OUT, DT, KL, 1024, 19, true, false, true>(a, st);
     }
     // Rows past the registers, online: float32 holds the row's first four
     // chunks (64 registers a thread) in registers, the next part in LDS, and
     // streams the rest twice.
     if constexpr (DT == kF32)
-        return launch_one<DT, KL, 1024, 0, true, false, false, 4>(a, st);
+        return launch_one<OUT, DT, KL, 1024, 0, true, false, false, 4>(a, st);
     else
-        return launch_one<DT, KL, 1024, 0, true>(a, st);
+        return launch_one<OUT, DT, KL, 1024, 0, true>(a, st);
 }
 
 }  // namespace
 
-hipError_t launch_rows(int dtype, bool kl, const RowArgs &a, hipStream_t st)
+hipError_t launch_rows(int dtype, bool kl, const RowArgs &a, hipStream_t st, int out)
 {
     const size_t elt = dtype == kF32 ? 4 : 2;
     const int n = 16 / (int)elt;
-    const bool vec = ((uintptr_t)a.logits % 16 == 0) && (a.V % n == 0);
+    bool vec = ((uintptr_t)a.logits % 16 == 0) && (a.V % n == 0);
+    if (out != 0) {
+        // half-precision gradient rows: float32 KL rows only; vector stores
+        // of 4 halves need 8-byte aligned output rows
+        if (dtype != kF32 || !kl || !a.gout)
+            return hipErrorInvalidValue;
+        vec = vec && ((uintptr_t)a.gout % 8 == 0);
+        return out == 1 ? launch_dt<kF32, true, 1>(a, st, vec) : launch_dt<kF32, true, 2>(a, st, vec);
+    }
     if (dtype == kF32)
-        return kl ? launch_dt<kF32, true>(a, st, vec) : launch_dt<kF32, false>(a, st, vec);
-    return kl ? launch_dt<kBF16, true>(a, st, vec) : launch_dt<kBF16, false>(a, st, vec);
+        return kl ? launch_dt<kF32, true, 0>(a, st, vec) : launch_dt<kF32, false, 0>(a, st, vec);
+    return kl ? launch_dt<kBF16, true, 0>(a, st, vec) : launch_dt<kBF16, false, 0>(a, st, vec);
 }
 
 }  // namespace vl
