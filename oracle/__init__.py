@@ -12,6 +12,7 @@ patterns.  Labels and ids are read as uint32.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 import threading
@@ -223,3 +224,115 @@ def head_kl(x, w, ids, probs, total, gscale):
     d *= coef
     dx = (d @ w) / float(gscale)
     return loss, dx
+
+
+# ---------------------------------------------------- vocabulary slices
+
+def _widen(logits) -> np.ndarray:
+    """[n][w] float32 or bf16 bit patterns (uint16) as exact float64."""
+    a = _rows2d(logits)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype != np.float32:
+        raise TypeError(f"oracle logits must be float32 or uint16 (bf16 bits), got {a.dtype}")
+    return a.astype(np.float64)
+
+
+def _in_range(n, rng):
+    if rng is None:
+        return np.ones(n, dtype=bool)
+    seq_len, start, end = rng
+    pos = np.arange(n) % int(seq_len)
+    return (pos >= int(start)) & (pos < int(end))
+
+
+def kl_slice_part(slice_logits, off, ids, probs, rng=None):
+    """Partial statistics of one vocabulary slice for the distillation KL
+    (cortiq-engine train_head.rs: the module doc's loss, and the head's
+    vocabulary cuts, each a column offset and a width).  The slice holds
+    columns [off, off + width) of each row; per row, in float64:
+
+      a = max of the slice's values (0 if it has no finite value)
+      z = sum_j exp(s_j - a)
+      P = sum of p_q over the teacher entries with off <= id_q < off + width
+          and p_q > 0
+      w = sum over the same entries of p_q (ln p_q - (s[id_q - off] - a))
+
+    Rows outside the loss range get (0, 0, 0, 0).  Returns [n][4].
+    """
+    s = _widen(slice_logits)
+    n, width = s.shape
+    idv = np.ascontiguousarray(ids).astype(np.int64).reshape(n, -1)
+    pv = np.ascontiguousarray(probs, dtype=np.float32).astype(np.float64).reshape(n, -1)
+    live = _in_range(n, rng)
+    out = np.zeros((n, 4))
+    for t in range(n):
+        if not live[t]:
+            continue
+        row = s[t]
+        fin = row[np.isfinite(row)]
+        a = float(fin.max()) if fin.size else 0.0
+        z = float(np.exp(row - a).sum())
+        P = 0.0
+        w = 0.0
+        for q in range(idv.shape[1]):
+            j, p = idv[t, q] - off, pv[t, q]
+            if 0 <= j < width and p > 0.0:
+                P += p
+                w += p * (math.log(p) - (row[j] - a))
+        out[t] = (a, z, P, w)
+    return out
+
+
+def kl_slice_merge(parts, rng=None):
+    """Loss and logsumexp of whole rows from the partial statistics of every
+    slice of the vocabulary (``parts`` [S][n][4], as ``kl_slice_part``
+    gives them), float64:
+
+      lse  = ln sum_i z_i e^{a_i}      over the slices with z_i > 0
+      loss = sum_i (w_i + P_i (lse - a_i))   over the slices with P_i > 0
+
+    which is sum_q p_q (ln p_q - s_{id_q} + lse), the KL of the whole row,
+    because the slices partition the vocabulary.  Rows outside the loss range
+    get loss 0 and lse 0.  Returns (loss [n], lse [n]).
+    """
+    pa = np.asarray(parts, dtype=np.float64)
+    S, n, _ = pa.shape
+    live = _in_range(n, rng)
+    loss = np.zeros(n)
+    lse = np.zeros(n)
+    for t in range(n):
+        if not live[t]:
+            continue
+        a, z, P, w = pa[:, t, 0], pa[:, t, 1], pa[:, t, 2], pa[:, t, 3]
+        has = z > 0.0
+        M = float(a[has].max())
+        L = M + math.log(float((z[has] * np.exp(a[has] - M)).sum()))
+        lse[t] = L
+        tgt = P > 0.0
+        loss[t] = float((w[tgt] + P[tgt] * (L - a[tgt])).sum())
+    return loss, lse
+
+
+def kl_slice_bwd(slice_logits, off, ids, probs, lse, coef=1.0, rng=None):
+    """Gradient of one vocabulary slice from the rows' logsumexp, used as
+    given: g_j = coef (exp(s_j - lse) - t_j), t_j = p_q where id_q = off + j
+    (else 0), the module doc's p_S - p_T restricted to the slice.  Rows
+    outside the loss range get 0.  Returns [n][width] float64."""
+    s = _widen(slice_logits)
+    n, width = s.shape
+    idv = np.ascontiguousarray(ids).astype(np.int64).reshape(n, -1)
+    pv = np.ascontiguousarray(probs, dtype=np.float32).astype(np.float64).reshape(n, -1)
+    L = np.asarray(lse, dtype=np.float64).reshape(-1)
+    live = _in_range(n, rng)
+    g = np.zeros((n, width))
+    for t in range(n):
+        if not live[t]:
+            continue
+        d = np.exp(s[t] - L[t])
+        for q in range(idv.shape[1]):
+            j = idv[t, q] - off
+            if 0 <= j < width:
+                d[j] -= pv[t, q]
+        g[t] = float(coef) * d
+    return g

@@ -582,3 +582,124 @@ def test_round_half_is_round_to_nearest_even():
     np.testing.assert_array_equal(oracle.round_half(tie, "bf16"), [1.0, 1.0 + 2**-6, -1.0])
     assert oracle.round_half(np.float32(1.0 + 2.0**-11), "f16") == 1.0
     assert oracle.round_half(one, "bf16") == 1.0
+
+
+# ------------------------------------------------ vocabulary slices (KL)
+
+def _cuts(V, widths):
+    offs = np.cumsum([0] + list(widths))
+    assert offs[-1] == V
+    return [(int(o), int(w)) for o, w in zip(offs[:-1], widths)]
+
+
+def _sliced(x, ids, p, cuts, rng=None):
+    parts = [oracle.kl_slice_part(x[:, o:o + w], o, ids, p, rng=rng) for o, w in cuts]
+    return parts, oracle.kl_slice_merge(parts, rng=rng)
+
+
+def test_kl_slices_merge_to_the_whole_row_kl():
+    """Merged slice statistics give the whole-row KL and logsumexp of the C
+    routine (written separately), for ragged cuts and a loss range; the
+    slice gradients from that lse are the whole-row gradient's columns."""
+    n, V, k = 9, 1000, 24
+    x = rows_f32(n, V, 3.0)
+    ids = distinct(n, V, k)
+    p = renorm_probs(n, k)
+    rng = (3, 1, 3)
+    for widths in ((V,), (500, 500), (333, 367, 300), (1, 998, 1), (64,) * 15 + (40,)):
+        cuts = _cuts(V, widths)
+        _, (loss, lse) = _sliced(x, ids, p, cuts, rng=rng)
+        wl, wlse, wg = oracle.kl(x, ids, p, rng=rng, coef=0.625)
+        np.testing.assert_allclose(loss, wl, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse, wlse, rtol=1e-13, atol=0)
+        g = np.concatenate([oracle.kl_slice_bwd(x[:, o:o + w], o, ids, p, wlse, coef=0.625,
+                                                rng=rng) for o, w in cuts], axis=1)
+        np.testing.assert_allclose(g, wg, rtol=1e-12, atol=1e-16)
+
+
+def test_kl_slices_bf16_merge_to_the_whole_row_kl():
+    n, V, k = 4, 640, 32
+    b = f32_to_bf16_bits(rows_f32(n, V))
+    ids = distinct(n, V, k)
+    p = renorm_probs(n, k)
+    _, (loss, lse) = _sliced(b, ids, p, _cuts(V, (320, 320)))
+    wl, wlse, _ = oracle.kl(b, ids, p, want_grad=False)
+    np.testing.assert_allclose(loss, wl, rtol=1e-12)
+    np.testing.assert_allclose(lse, wlse, rtol=1e-13)
+
+
+def test_kl_slice_part_closed_forms():
+    # constant slice, no teacher entry in it: a = c, z = width exactly, P = w = 0
+    x = np.full((2, 50), 1.75, dtype=np.float32)
+    ids = np.array([[0, 1], [2, 3]], dtype=np.uint32)
+    p = np.full((2, 2), 0.5, dtype=np.float32)
+    part = oracle.kl_slice_part(x, 100, ids, p)
+    np.testing.assert_array_equal(part, [[1.75, 50.0, 0.0, 0.0]] * 2)
+    # one teacher entry of probability 1 at the slice's maximum: w = 0, P = 1
+    y = np.array([[0.0, 3.0, -1.0]], dtype=np.float32)
+    part = oracle.kl_slice_part(y, 7, np.array([[8]], np.uint32), np.array([[1.0]], np.float32))
+    assert part[0, 0] == 3.0 and part[0, 2] == 1.0 and part[0, 3] == 0.0
+    assert abs(part[0, 1] - (1.0 + math.exp(-3.0) + math.exp(-4.0))) < 1e-15
+
+
+def test_kl_slices_uniform_closed_form():
+    """Uniform student over V, uniform teacher over k ids spread over three
+    slices: KL = ln(V / k)."""
+    V, k = 96, 8
+    x = np.full((1, V), -2.0, dtype=np.float32)
+    ids = np.array([[0, 5, 31, 32, 40, 63, 64, 95]], dtype=np.uint32)
+    p = np.full((1, k), 1.0 / k, dtype=np.float32)
+    _, (loss, lse) = _sliced(x, ids, p, _cuts(V, (32, 32, 32)))
+    assert abs(loss[0] - math.log(V / k)) < 1e-13
+    assert abs(lse[0] - (-2.0 + math.log(V))) < 1e-13
+
+
+def test_kl_slices_unit_target_is_the_cross_entropy():
+    """k = 1, p = 1 over slices gives the C cross-entropy routine's loss and
+    gradient."""
+    n, V = 6, 301
+    x = rows_f32(n, V)
+    lab = RNG.integers(0, V, size=n).astype(np.uint32)
+    one = np.ones((n, 1), np.float32)
+    cuts = _cuts(V, (100, 101, 100))
+    _, (loss, lse) = _sliced(x, lab[:, None], one, cuts)
+    wl, wlse, wg = oracle.ce(x, lab, scale=0.5)
+    np.testing.assert_allclose(loss, wl, rtol=1e-12, atol=1e-14)
+    g = np.concatenate([oracle.kl_slice_bwd(x[:, o:o + w], o, lab[:, None], one, lse, coef=0.5)
+                        for o, w in cuts], axis=1)
+    np.testing.assert_allclose(g, wg, rtol=1e-12, atol=1e-16)
+
+
+def test_kl_slice_of_minus_inf_is_left_out():
+    """A slice with no finite value and no teacher entry has z = 0, a = 0
+    and leaves the merge unchanged."""
+    n, V, k = 3, 60, 4
+    x = rows_f32(n, V)
+    x[:, 20:40] = -np.inf
+    ids = np.array([[0, 1, 45, 59], [2, 3, 4, 5], [41, 42, 43, 44]], dtype=np.uint32)
+    p = renorm_probs(n, k)
+    parts, (loss, lse) = _sliced(x, ids, p, _cuts(V, (20, 20, 20)))
+    np.testing.assert_array_equal(parts[1], np.zeros((n, 4)))
+    wl, wlse, _ = oracle.kl(x, ids, p, want_grad=False)
+    np.testing.assert_allclose(loss, wl, rtol=1e-12)
+    np.testing.assert_allclose(lse, wlse, rtol=1e-13)
+
+
+def test_kl_slices_finite_differences():
+    """Central differences of the merged loss in every logit equal the slice
+    gradients formed from the merged lse (coef 1)."""
+    h = 2.0 ** -12
+    V, k = 12, 4
+    x = rows_f32(1, V, 1.5)
+    ids = np.array([[0, 5, 6, 11]], dtype=np.uint32)
+    p = renorm_probs(1, k)
+    cuts = _cuts(V, (5, 7))
+    _, (_, lse) = _sliced(x, ids, p, cuts)
+    g = np.concatenate([oracle.kl_slice_bwd(x[:, o:o + w], o, ids, p, lse)
+                        for o, w in cuts], axis=1)
+    for j in range(V):
+        xp = x.copy(); xp[0, j] += np.float32(h)
+        xm = x.copy(); xm[0, j] -= np.float32(h)
+        lp = _sliced(xp, ids, p, cuts)[1][0][0]
+        lm = _sliced(xm, ids, p, cuts)[1][0][0]
+        assert abs((lp - lm) / (2 * h) - g[0, j]) < 1e-7
