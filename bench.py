@@ -18,7 +18,7 @@ Prints one JSON line.  `value` is logits rows per second of the whole step;
 the launch stream around every launch of the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-                    [--workload step|ce_lm|ce_split|topk_zipf|kl_large|kl_bf16|head_kl|
+                    [--workload step|ce_lm|ce_split|topk_zipf|kl_large|kl_bf16|kl_sliced|head_kl|
                                 copy_calib]
     python bench.py --pmc-summary <counter_collection.csv> ...
 
@@ -188,6 +188,44 @@ def other_workload(name, dev):
                   "acc": 3 * ntok * hs * 4}
         cfg = {"workload": gi.KL_BF16.name, "ntok": ntok, "V": V, "k": k, "dtype": "bf16",
                "bytes_model": "KL 1R+1W"}
+    elif name == "kl_sliced":
+        # the same bf16 workload as two vocabulary slices of 75968, each its
+        # own [ntok][75968] buffer: statistics of each slice, the merge, the
+        # gradient of each slice from the merged lse, then the slice
+        # accumulate of the two slices' input gradients
+        c = gi.kl_bf16_sliced(dev)
+        x, t, k = c["logits"], c["teacher"], c["k"]
+        ntok, V = x.shape
+        hs = c["dh0"].shape[1]
+        ids = torch.empty((ntok, k), dtype=torch.int32, device=dev)
+        probs = torch.empty((ntok, k), device=dev)
+        vl.vl_topk_renorm(t, k, ids, probs)
+        del t, c["teacher"]
+        w = V // 2
+        sl = [x[:, :w].contiguous(), x[:, w:].contiguous()]
+        del x, c["logits"]
+        parts = torch.empty((2, ntok, 4), device=dev)
+        loss = torch.empty(ntok, device=dev)
+        lse = torch.empty(ntok, device=dev)
+        calls = [("part0", lambda: vl.vl_kl_slice_fwd(sl[0], 0, ids, probs, parts[0])),
+                 ("part1", lambda: vl.vl_kl_slice_fwd(sl[1], w, ids, probs, parts[1])),
+                 ("merge", lambda: vl.vl_kl_slice_merge(parts, loss, lse)),
+                 ("bwd0", lambda: vl.vl_kl_slice_bwd(sl[0], 0, ids, probs, lse,
+                                                     coef=c["coef"])),
+                 ("bwd1", lambda: vl.vl_kl_slice_bwd(sl[1], w, ids, probs, lse,
+                                                     coef=c["coef"])),
+                 ("acc", lambda: vl.vl_slice_acc(c["dh0"], c["dh1"]))]
+        # the part pass reads its slice once; the gradient pass reads and
+        # writes it; ids and probs are read by each pass of each slice
+        nbytes = {"part0": ntok * w * 2 + ntok * k * 8 + ntok * 16,
+                  "part1": ntok * w * 2 + ntok * k * 8 + ntok * 16,
+                  "merge": 2 * ntok * 16 + ntok * 8,
+                  "bwd0": ntok * 2 * w * 2 + ntok * k * 8 + ntok * 4,
+                  "bwd1": ntok * 2 * w * 2 + ntok * k * 8 + ntok * 4,
+                  "acc": 3 * ntok * hs * 4}
+        cfg = {"workload": gi.KL_BF16.name + ", two vocabulary slices of 75968 in separate "
+                           "buffers", "ntok": ntok, "V": V, "k": k, "dtype": "bf16",
+               "bytes_model": "slice statistics 1R, slice gradient 1R+1W"}
     elif name == "head_kl":
         # the vocabulary head around the KL: two GEMMs of 2 ntok V hs flops
         # each on the matrix cores, the KL rows and two conversions between

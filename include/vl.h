@@ -170,6 +170,58 @@ int vl_topk_renorm(const void *logits, int dtype, int64_t ntok, int64_t V, int64
 int vl_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream);
 
 /*
+ * The distillation KL over a vocabulary split into slices [KL: module doc
+ * (loss and gradient p_S - p_T); Head (the vocabulary cut into column
+ * slices, each an offset and a width); head_kl (one product per slice)].
+ * Each slice is a block of logits of its own, so no buffer of whole rows is
+ * needed; the same three calls serve a vocabulary sharded over devices
+ * (exchange the parts, 16 bytes per row and slice, then merge).
+ *
+ * vl_kl_slice_fwd -- statistics of one slice, one read of it.
+ *   logits  slice rows, dtype, read only: row r holds vocabulary ids
+ *           [off, off + width) at elements r * ld + [0, width).
+ *   ld      row stride in elements, >= width (width for a dense block).
+ *   off     vocabulary id of the slice's first column, >= 0.
+ *   ids     [ntok][k] uint32, probs [ntok][k] float32, read only: the
+ *           teacher's ids and probabilities over the whole vocabulary; each
+ *           slice uses the entries whose id falls into it.
+ *   part    [ntok][4] float32, written, 16-byte aligned: per row
+ *             a = max of the slice's values (0 if none is finite),
+ *             z = sum_j exp(s_j - a),
+ *             P = sum of probs[q] > 0 whose id is in the slice,
+ *             w = sum over those q of probs[q] (ln probs[q] - (s_id - a)).
+ *           Rows outside the loss range get (0, 0, 0, 0) and are not read.
+ * vl_kl_slice_merge -- the whole rows' loss and logsumexp from the parts of
+ * every slice (the slices must partition [0, V) and the parts be written
+ * with the same rng).
+ *   parts   [nslice][ntok][4] float32, read only, 16-byte aligned: the
+ *           nslice slices' part buffers back to back.
+ *   loss    [ntok] float32, written: sum over slices with P > 0 of
+ *           w + P (lse - a), which is vl_kl_fwd_bwd's loss of the whole row.
+ *   lse     [ntok] float32 or NULL, written: ln sum over slices with z > 0
+ *           of z exp(a).
+ *   Rows outside the loss range get loss 0 and lse 0.
+ * vl_kl_slice_bwd -- the gradient of one slice, one read and one write.
+ *   logits  as for vl_kl_slice_fwd; in: the logits, out: the gradient
+ *           coef (exp(s_j - lse) - t_j), t_j = probs[q] where ids[q] = off + j,
+ *           stored in dtype.
+ *   lse     [ntok] float32, read only: the merged logsumexp, used as given.
+ *   Rows outside the loss range are set to 0 and not read.
+ * Cross-entropy over slices is the same calls with k = 1, ids = labels and
+ * probs = 1.
+ * Limits: 1 <= width, off + width <= 2^31 - 1, ld >= width, k >= 1,
+ * nslice >= 1.  Ids outside every slice contribute nothing.
+ */
+int vl_kl_slice_fwd(const void *logits, int dtype, int64_t ld, int64_t off, int64_t width,
+                    const uint32_t *ids, const float *probs, int64_t k, float *part,
+                    int64_t ntok, const vl_range *rng, hipStream_t stream);
+int vl_kl_slice_merge(const float *parts, int64_t nslice, float *loss, float *lse,
+                      int64_t ntok, const vl_range *rng, hipStream_t stream);
+int vl_kl_slice_bwd(void *logits, int dtype, int64_t ld, int64_t off, int64_t width,
+                    const uint32_t *ids, const float *probs, int64_t k, const float *lse,
+                    int64_t ntok, const vl_range *rng, float coef, hipStream_t stream);
+
+/*
  * Scratch bytes vl_head_kl needs for `chunk` rows at a time: float32 logits
  * [chunk][V], the half-precision hidden rows [chunk][hs] and gradient
  * [chunk][V], and a 64 MiB GEMM workspace, each 256-byte aligned.

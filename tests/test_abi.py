@@ -25,11 +25,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(vl_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_ten_calls():
+def test_header_declares_the_thirteen_calls():
     assert declared_functions() == sorted(
         ["vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
          "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
-         "vl_strerror"])
+         "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -189,3 +189,55 @@ def test_head_host_checks(lib):
     for name in ("x", "w", "ids", "probs", "dx", "loss", "scratch"):
         assert call(**{name: None}) == VL_EINVAL, name
     assert call(ntok=0, x=None, scratch=None) == VL_OK
+
+
+P16 = ctypes.c_void_p(0x2000)  # 16-byte aligned, never dereferenced
+P4 = ctypes.c_void_p(0x2004)   # 4-byte aligned only
+
+
+def slice_fwd(lib, **kw):
+    a = dict(logits=P, dtype=0, ld=16, off=0, width=16, ids=P, probs=P, k=2, part=P16,
+             ntok=4, rng=None, stream=None)
+    a.update(kw)
+    return lib.vl_kl_slice_fwd(a["logits"], a["dtype"], a["ld"], a["off"], a["width"],
+                               a["ids"], a["probs"], a["k"], a["part"], a["ntok"], a["rng"],
+                               a["stream"])
+
+
+def slice_bwd(lib, **kw):
+    a = dict(logits=P, dtype=0, ld=16, off=0, width=16, ids=P, probs=P, k=2, lse=P,
+             ntok=4, rng=None, coef=1.0, stream=None)
+    a.update(kw)
+    return lib.vl_kl_slice_bwd(a["logits"], a["dtype"], a["ld"], a["off"], a["width"],
+                               a["ids"], a["probs"], a["k"], a["lse"], a["ntok"], a["rng"],
+                               a["coef"], a["stream"])
+
+
+def test_slice_host_checks(lib):
+    for f in (slice_fwd, slice_bwd):
+        assert f(lib, dtype=2) == VL_EDTYPE
+        assert f(lib, width=0) == VL_EINVAL
+        assert f(lib, ld=15) == VL_EINVAL  # rows would overlap
+        assert f(lib, off=-1) == VL_EINVAL
+        assert f(lib, off=(1 << 31) - 16) == VL_EINVAL  # off + width past 2^31 - 1
+        assert f(lib, k=0) == VL_EINVAL
+        assert f(lib, ntok=-1) == VL_EINVAL
+        assert f(lib, ntok=1 << 62, ld=1 << 20, width=1 << 20) == VL_EINVAL
+        assert f(lib, rng=rng(4, 3, 2)) == VL_EINVAL
+        for name in ("logits", "ids", "probs"):
+            assert f(lib, **{name: None}) == VL_EINVAL, name
+        assert f(lib, ntok=0, logits=None, ids=None, probs=None) == VL_OK
+    assert slice_fwd(lib, part=None) == VL_EINVAL
+    assert slice_fwd(lib, part=P4) == VL_EINVAL  # parts are 16-byte records
+    assert slice_bwd(lib, lse=None) == VL_EINVAL
+
+
+def test_slice_merge_host_checks(lib):
+    f = lib.vl_kl_slice_merge
+    assert f(P16, 0, P, None, 4, None, None) == VL_EINVAL
+    assert f(P16, 2, P, None, -1, None, None) == VL_EINVAL
+    assert f(None, 2, P, None, 4, None, None) == VL_EINVAL
+    assert f(P4, 2, P, None, 4, None, None) == VL_EINVAL
+    assert f(P16, 2, None, None, 4, None, None) == VL_EINVAL
+    assert f(P16, 2, P, None, 4, rng(0, 0, 0), None) == VL_EINVAL
+    assert f(None, 2, None, None, 0, None, None) == VL_OK

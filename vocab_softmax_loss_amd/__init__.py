@@ -23,7 +23,8 @@ import torch
 __all__ = [
     "VL_F32", "VL_BF16", "VL_F16", "VLError", "lib_path",
     "vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
-    "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl", "vl_strerror",
+    "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
+    "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -65,10 +66,14 @@ def _load():
     lib.vl_head_kl.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, i64, i64, i64, i64, f32, i64,
                                vp, ctypes.c_size_t, vp]
     lib.vl_head_kl.restype = i32
+    lib.vl_kl_slice_fwd.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp, i64, rp, vp]
+    lib.vl_kl_slice_merge.argtypes = [vp, i64, vp, vp, i64, rp, vp]
+    lib.vl_kl_slice_bwd.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp, i64, rp, f32, vp]
     lib.vl_strerror.argtypes = [i32]
     lib.vl_strerror.restype = ctypes.c_char_p
     for f in (lib.vl_ce_fwd_bwd, lib.vl_ce_fwd, lib.vl_ce_bwd, lib.vl_loss_mean,
-              lib.vl_kl_fwd_bwd, lib.vl_topk_renorm, lib.vl_slice_acc):
+              lib.vl_kl_fwd_bwd, lib.vl_topk_renorm, lib.vl_slice_acc, lib.vl_kl_slice_fwd,
+              lib.vl_kl_slice_merge, lib.vl_kl_slice_bwd):
         f.restype = i32
     return lib
 
@@ -233,3 +238,63 @@ def vl_head_kl(x, w, ids, probs, dx, loss, total, gscale, chunk, scratch, stream
             ntok, V, hs, int(total), float(gscale), int(chunk),
             _dev(scratch, "scratch", (torch.uint8,)), scratch.numel(),
             _stream(x, stream)), "vl_head_kl")
+
+
+def _slice_rows(t: torch.Tensor, name: str):
+    """Pointer and row stride of a [ntok][width] slice whose rows may be a
+    column window of a wider buffer (element stride 1, row stride >= width)."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    ntok, width = t.shape
+    if width > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    ld = t.stride(0) if ntok > 1 else width
+    if ld < width:
+        raise ValueError(f"{name} rows overlap (row stride {ld} < width {width})")
+    return t.data_ptr(), int(ld)
+
+
+def vl_kl_slice_fwd(logits, off, ids, probs, part, rng=None, stream=None):
+    """Statistics (a, z, P, w) of one vocabulary slice; see vl_kl_slice_fwd.
+    ``logits`` [ntok][width] holds vocabulary ids [off, off + width); it may
+    be a column window of a wider tensor.  ``part`` is a [ntok][4]
+    float32 tensor."""
+    ntok, width = logits.shape
+    k = ids.shape[1] if ids.dim() == 2 else 0
+    ptr, ld = _slice_rows(logits, "logits")
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_kl_slice_fwd(
+            ptr, _dtype_code(logits), ld, int(off), width,
+            _dev(ids, "ids", _INT_IDS, (ntok, k)),
+            _dev(probs, "probs", (torch.float32,), (ntok, k)), k,
+            _dev(part, "part", (torch.float32,), (ntok, 4)),
+            ntok, _range(rng), _stream(logits, stream)), "vl_kl_slice_fwd")
+
+
+def vl_kl_slice_merge(parts, loss, lse=None, rng=None, stream=None):
+    """Whole-row loss and lse from every slice's part ([nslice][ntok][4]
+    float32); see vl_kl_slice_merge."""
+    nslice, ntok = parts.shape[0], parts.shape[1]
+    with torch.cuda.device(parts.device):
+        _check(_lib.vl_kl_slice_merge(
+            _dev(parts, "parts", (torch.float32,), (nslice, ntok, 4)), nslice,
+            _dev(loss, "loss", (torch.float32,), (ntok,)),
+            None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, _range(rng), _stream(parts, stream)), "vl_kl_slice_merge")
+
+
+def vl_kl_slice_bwd(logits, off, ids, probs, lse, rng=None, coef=1.0, stream=None):
+    """Gradient of one vocabulary slice from the merged lse, written over
+    the slice; see vl_kl_slice_bwd."""
+    ntok, width = logits.shape
+    k = ids.shape[1] if ids.dim() == 2 else 0
+    ptr, ld = _slice_rows(logits, "logits")
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_kl_slice_bwd(
+            ptr, _dtype_code(logits), ld, int(off), width,
+            _dev(ids, "ids", _INT_IDS, (ntok, k)),
+            _dev(probs, "probs", (torch.float32,), (ntok, k)), k,
+            _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, _range(rng), float(coef), _stream(logits, stream)), "vl_kl_slice_bwd")

@@ -257,6 +257,83 @@ int vl_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream)
     return status_of(vl::launch_slice_acc(dst, src, n, stream));
 }
 
+// Shared checks of the two slice passes; fills `a` except the pass's own
+// pointers.
+static int check_slice(const void *logits, int dtype, int64_t ld, int64_t off, int64_t width,
+                       const uint32_t *ids, const float *probs, int64_t k, int64_t ntok,
+                       const vl_range *rng, vl::SliceArgs &a)
+{
+    vl::RowArgs r{};
+    int st = check_rows(dtype, ntok, width, rng, r);
+    if (st != VL_OK)
+        return st;
+    if (ld < width || off < 0 || off > kMaxV - width || k < 1)
+        return VL_EINVAL;
+    if (ntok > INT64_MAX / ld || ntok > INT64_MAX / k)
+        return VL_EINVAL;
+    if (ntok > 0 && (!logits || !ids || !probs))
+        return VL_EINVAL;
+    a.logits = const_cast<void *>(logits);
+    a.ids = ids;
+    a.probs = probs;
+    a.ntok = ntok;
+    a.ld = ld;
+    a.off = off;
+    a.width = width;
+    a.k = k;
+    a.walk = r.walk;
+    return VL_OK;
+}
+
+int vl_kl_slice_fwd(const void *logits, int dtype, int64_t ld, int64_t off, int64_t width,
+                    const uint32_t *ids, const float *probs, int64_t k, float *part,
+                    int64_t ntok, const vl_range *rng, hipStream_t stream)
+{
+    vl::SliceArgs a{};
+    int st = check_slice(logits, dtype, ld, off, width, ids, probs, k, ntok, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (ntok == 0)
+        return VL_OK;
+    if (!part || (uintptr_t)part % 16 != 0)
+        return VL_EINVAL;
+    a.part = part;
+    return status_of(vl::launch_slice_part(dtype, a, stream));
+}
+
+int vl_kl_slice_merge(const float *parts, int64_t nslice, float *loss, float *lse,
+                      int64_t ntok, const vl_range *rng, hipStream_t stream)
+{
+    vl::RowArgs r{};
+    int st = check_rows(VL_F32, ntok, 1, rng, r);
+    if (st != VL_OK)
+        return st;
+    if (nslice < 1 || ntok > INT64_MAX / 16 / nslice)
+        return VL_EINVAL;
+    if (ntok == 0)
+        return VL_OK;
+    if (!parts || (uintptr_t)parts % 16 != 0 || !loss)
+        return VL_EINVAL;
+    return status_of(vl::launch_slice_merge(parts, nslice, ntok, r.walk, loss, lse, stream));
+}
+
+int vl_kl_slice_bwd(void *logits, int dtype, int64_t ld, int64_t off, int64_t width,
+                    const uint32_t *ids, const float *probs, int64_t k, const float *lse,
+                    int64_t ntok, const vl_range *rng, float coef, hipStream_t stream)
+{
+    vl::SliceArgs a{};
+    int st = check_slice(logits, dtype, ld, off, width, ids, probs, k, ntok, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (ntok == 0)
+        return VL_OK;
+    if (!lse)
+        return VL_EINVAL;
+    a.lse = lse;
+    a.coef = coef;
+    return status_of(vl::launch_slice_bwd(dtype, a, stream));
+}
+
 const char *vl_strerror(int status)
 {
     switch (status) {

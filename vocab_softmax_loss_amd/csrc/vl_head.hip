@@ -241,9 +241,9 @@ bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int
         }
     }
     if (e0)
-        hipEventDestroy(e0);
+        (void)hipEventDestroy(e0);
     if (e1)
-        hipEventDestroy(e1);
+        (void)hipEventDestroy(e1);
     if (best < 0)
         best = 0;
     {

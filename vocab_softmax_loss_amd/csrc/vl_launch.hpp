@@ -92,6 +92,18 @@ struct RowArgs {
     void *gout;               // out != 0: [ntok][V] half-precision gradient rows
 };
 
+// One call of the per-slice KL passes (checked by the caller).
+struct SliceArgs {
+    void *logits;           // row r of the slice starts at element r * ld
+    const uint32_t *ids;    // [ntok][k]
+    const float *probs;     // [ntok][k]
+    float *part;            // part pass: [ntok][4], 16-byte aligned
+    const float *lse;       // gradient pass: [ntok]
+    int64_t ntok, ld, off, width, k;
+    RowWalk walk;           // loss range as a row order
+    float coef;             // gradient scale
+};
+
 struct TopkArgs {
     const void *logits;  // [ntok][V]
     int64_t ntok, V, k;
@@ -132,6 +144,14 @@ hipError_t launch_ce_bwd(int dtype, const RowArgs &a, hipStream_t stream);
 // mean[0] = (sum of loss[0..n)) / count, or 0 when count is 0.
 hipError_t launch_loss_mean(const float *loss, int64_t n, int64_t count, float *mean,
                             hipStream_t stream);
+
+// The vocabulary-slice KL: per-row statistics of one slice, their merge
+// over nslice slices ([nslice][ntok][4]) into loss and lse (lse may be
+// null), and one slice's gradient from lse.
+hipError_t launch_slice_part(int dtype, const SliceArgs &a, hipStream_t stream);
+hipError_t launch_slice_merge(const float *parts, int64_t nslice, int64_t ntok,
+                              const RowWalk &walk, float *loss, float *lse, hipStream_t stream);
+hipError_t launch_slice_bwd(int dtype, const SliceArgs &a, hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_cus();
