@@ -85,6 +85,28 @@ __global__ __launch_bounds__(BLOCK) void slice_part_kernel(SliceArgs a)
     for (; c.j < w.n_in; c.advance(), par ^= 1) {
         const int64_t row = c.in_row(w);
         const char *p = slice_row<DT>(a.logits, row, a.ld);
+        // Teacher entries of this row that fall into the slice, gathered
+        // before the row is streamed: the lines they touch then sit in the
+        // cache when the streaming loads reach them (gathered afterwards,
+        // each cost a line fetched a second time, 11% of the slice at
+        // k = 256).  The first QR * BLOCK entries wait in registers until
+        // the anchor is known; any further ones are gathered afterwards.
+        constexpr int QR = 4;
+        float gp[QR], gs[QR];
+#pragma unroll
+        for (int r = 0; r < QR; ++r) {
+            const int64_t q = (int64_t)tid + (int64_t)r * BLOCK;
+            gp[r] = 0.f;
+            gs[r] = 0.f;
+            if (q < a.k) {
+                const int64_t j = (int64_t)a.ids[row * a.k + q] - a.off;
+                const float pq = a.probs[row * a.k + q];
+                if (j >= 0 && j < (int64_t)width && pq > 0.f) {
+                    gp[r] = pq;
+                    gs[r] = IO::load_elem(p, (uint32_t)j);
+                }
+            }
+        }
         float m = -INFINITY, s = 0.f;
         for (uint32_t v0 = tid; v0 < nvec; v0 += (uint32_t)BLOCK * U) {
             Raw y[U];
@@ -141,16 +163,20 @@ __global__ __launch_bounds__(BLOCK) void slice_part_kernel(SliceArgs a)
         // a slice with no finite value: anchor 0, z = 0 (the merge skips it)
         const float anchor = (M == -INFINITY) ? 0.f : M;
 
-        // teacher entries of this row that fall into the slice
         float tp = 0.f, tw = 0.f;
-        for (int64_t q = tid; q < a.k; q += BLOCK) {
-            const uint32_t id = a.ids[row * a.k + q];
+#pragma unroll
+        for (int r = 0; r < QR; ++r) {
+            if (gp[r] > 0.f) {
+                tp += gp[r];
+                tw += gp[r] * (__logf(gp[r]) - (gs[r] - anchor));
+            }
+        }
+        for (int64_t q = (int64_t)tid + (int64_t)QR * BLOCK; q < a.k; q += BLOCK) {
+            const int64_t j = (int64_t)a.ids[row * a.k + q] - a.off;
             const float pq = a.probs[row * a.k + q];
-            const int64_t j = (int64_t)id - a.off;
             if (j >= 0 && j < (int64_t)width && pq > 0.f) {
-                const float sj = IO::load_elem(p, (uint32_t)j);
                 tp += pq;
-                tw += pq * (__logf(pq) - (sj - anchor));
+                tw += pq * (__logf(pq) - (IO::load_elem(p, (uint32_t)j) - anchor));
             }
         }
         tp = wave_sum(tp);
