@@ -21,7 +21,7 @@
 //    once and written once (1R + 1W).  How the next row's reads overlap the
 //    current row depends on the shape: several blocks per CU (small
 //    blocks); an asynchronous copy of the next row into LDS (PF, one
-//    512-thread block per CU); or, for rows that fill a 1024-thread
+//    512- or 1024-thread block per CU); or, for rows that fill a 1024-thread
 //    block's registers, each register refilled with the next row's vector
 //    right after its gradient is stored (RL).  float32 keeps
 //    e = exp(s - m_thread) in place of s and stores e * coef *
@@ -786,11 +786,14 @@ hipError_t launch_dt(const RowArgs &a, hipStream_t st, bool vec)
             return launch_one<OUT, DT, KL, 256, 4, true>(a, st);
         if (nvec <= 2048)
             return launch_one<OUT, DT, KL, 256, 8, true>(a, st);
-        // One 512-thread block per CU, the next row streaming into LDS.
+        // One block per CU, the next row streaming into LDS.  At V = 32000
+        // 1024 threads x 8 vectors run the KL and CE 1.6-2.2% faster than
+        // 512 x 16 (the same 128 KB row, twice the waves to hide the
+        // reductions' latency).
         if (nvec <= 4096)
             return launch_one<OUT, DT, KL, 512, 8, true, true>(a, st);
         if (nvec <= 8192)
-            return launch_one<OUT, DT, KL, 512, 16, true, true>(a, st);
+            return launch_one<OUT, DT, KL, 1024, 8, true, true>(a, st);
     } else {
         // bf16 widens to twice its register footprint: at most 8 vectors
         // (64 values) per thread.
