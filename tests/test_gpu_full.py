@@ -46,6 +46,47 @@ def topk_invariants(x, ids, probs, k):
     assert float((probs.double().sum(dim=1) - 1).abs().max()) < 1e-5
 
 
+def test_bench_step_full(vl):
+    """The bench step exactly as bench.py times it (its inputs, calls and
+    arguments, 4096 x 32000 float32): teacher top-k, KL against it, the
+    prompt-masked CE, slice accumulate.  Every row against the oracle; the
+    KL both against the GPU's top-k (stage-isolated) and end to end from
+    the teacher bytes."""
+    import bench
+    x = bench.make_inputs(DEV)
+    host = bench.host_copies(x)
+    ntok, k = bench.NTOK, bench.K_TOPK
+    ids = torch.empty((ntok, k), dtype=torch.int32, device=DEV)
+    probs = torch.empty((ntok, k), device=DEV)
+    kl_loss = torch.empty(ntok, device=DEV)
+    ce_loss = torch.empty(ntok, device=DEV)
+    coef = 1024.0 / ntok
+    vl.vl_topk_renorm(x["teacher"], k, ids, probs)
+    vl.vl_kl_fwd_bwd(x["kl_student"], ids, probs, kl_loss, coef=coef)
+    vl.vl_ce_fwd_bwd(x["ce_logits"], x["labels"], ce_loss, rng=x["rng"], scale=x["scale"])
+    vl.vl_slice_acc(x["dh0"], x["dh1"])
+    torch.cuda.synchronize()
+    gi_ids = ids.cpu().numpy().view(np.uint32)
+    gi_p = probs.cpu().numpy()
+    kl_l, ce_l = kl_loss.cpu().numpy(), ce_loss.cpu().numpy()
+    for r0 in range(0, ntok, 512):
+        r1 = r0 + 512
+        oi, op = oracle.topk(host["teacher"][r0:r1], k)
+        check_topk(gi_ids[r0:r1], gi_p[r0:r1], oi, op)
+        ol, _, og = oracle.kl(host["kl_student"][r0:r1], gi_ids[r0:r1], gi_p[r0:r1], coef=coef)
+        check_loss(kl_l[r0:r1], ol, "f32")
+        check_grad(x["kl_student"][r0:r1].cpu().numpy(), og, "f32", coef)
+        el, _, _ = oracle.kl(host["kl_student"][r0:r1], oi, op.astype(np.float32), coef=coef,
+                             want_grad=False)
+        check_loss(kl_l[r0:r1], el, "f32", "KL end to end")
+        ol, _, og = oracle.ce(host["ce_logits"][r0:r1], host["labels"][r0:r1], rng=x["rng"],
+                              scale=x["scale"], row_index=np.arange(r0, r1))
+        check_loss(ce_l[r0:r1], ol, "f32")
+        check_grad(x["ce_logits"][r0:r1].cpu().numpy(), og, "f32", x["scale"])
+    want = oracle.acc(host["dh0"], host["dh1"])
+    assert np.array_equal(x["dh0"].cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
 def test_ce_lm_full(vl):
     """Cross-entropy, 8 x 512 tokens, V=32000, prompt mask: every row."""
     c = gi.ce_lm(DEV)
