@@ -204,9 +204,16 @@ def test_kl_bf16_sliced_full(vl):
     loss = torch.empty(ntok, device=DEV)
     vl.vl_kl_fwd_bwd(x, ids, probs, loss, coef=coef)
     torch.cuda.synchronize()
+    g = to_host_bytes(x[rows_t])
+    # stage-isolated: the oracle KL fed the GPU's own ids and probs
+    gid = ids[rows_t].cpu().numpy().view(np.uint32)
+    sl, _, sg = oracle.kl(xh, gid, probs[rows_t].cpu().numpy(), coef=coef)
+    check_loss(loss.cpu().numpy()[rows], sl, "bf16", "KL from the GPU's top-k")
+    check_grad(g, sg, "bf16", coef, "gradient from the GPU's top-k")
+    # end to end: the oracle's own top-k of the teacher bytes
     ol, _, og = oracle.kl(xh, oi, op.astype(np.float32), coef=coef)
     check_loss(loss.cpu().numpy()[rows], ol, "bf16")
-    check_grad(to_host_bytes(x[rows_t]), og, "bf16", coef)
+    check_grad(g, og, "bf16", coef)
 
     d0, d1 = c["dh0"], c["dh1"]
     want = oracle.acc(d0.cpu().numpy(), d1.cpu().numpy())
