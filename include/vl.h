@@ -250,8 +250,9 @@ size_t vl_head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
  * The two products run in hipBLASLt; its handle is created on the first
  * call on each device and kept until the process ends (the only allocation
  * the library makes).  The first call with a given shape on a device also
- * times up to 16 hipBLASLt algorithms for each product on `stream` and keeps
- * the fastest for later calls; that one call waits for the stream.  Under
+ * times up to 16 hipBLASLt algorithms for each product on `stream` (the
+ * three fastest a second time) and keeps the fastest for later calls; that
+ * one call waits for the stream.  Under
  * stream capture nothing is timed and hipBLASLt's first choice runs.
  * Limits: 1 <= k <= V <= 2^19, hs >= 1, chunk >= 1.
  * Returns VL_ELAUNCH if hipBLASLt finds no algorithm or rejects a call.

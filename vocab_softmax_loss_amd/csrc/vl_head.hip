@@ -225,6 +225,9 @@ bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int
     hipEvent_t e0 = nullptr, e1 = nullptr;
     int best = -1;
     float best_ms = 0.f;
+    float first_ms[kTuneCandidates];
+    for (int i = 0; i < kTuneCandidates; ++i)
+        first_ms[i] = -1.f;
     if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
         for (int i = 0; i < found; ++i) {
             if (res[i].workspaceSize > ws_bytes || !run(res[i].algo))
@@ -234,10 +237,53 @@ bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int
                 hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
                 hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
                 continue;
+            first_ms[i] = ms;
             if (best < 0 || ms < best_ms) {
                 best = i;
                 best_ms = ms;
             }
+        }
+    }
+    // The candidates often lie within a few percent of each other, inside
+    // the noise of two runs: time the three fastest again, in turns, four
+    // runs each, and keep the one with the least total.
+    if (best >= 0 && e0 && e1) {
+        int top[3] = {-1, -1, -1};
+        float top_ms[3] = {0.f, 0.f, 0.f};
+        for (int i = 0; i < found; ++i) {
+            if (first_ms[i] < 0.f)
+                continue;
+            for (int t = 0; t < 3; ++t) {
+                if (top[t] < 0 || first_ms[i] < top_ms[t]) {
+                    for (int u = 2; u > t; --u) {
+                        top[u] = top[u - 1];
+                        top_ms[u] = top_ms[u - 1];
+                    }
+                    top[t] = i;
+                    top_ms[t] = first_ms[i];
+                    break;
+                }
+            }
+        }
+        float total[3] = {0.f, 0.f, 0.f};
+        bool timed = true;
+        for (int r = 0; r < 4 && timed; ++r)
+            for (int t = 0; t < 3 && timed; ++t) {
+                if (top[t] < 0)
+                    continue;
+                float ms = 0.f;
+                timed = hipEventRecord(e0, st) == hipSuccess && run(res[top[t]].algo) &&
+                        hipEventRecord(e1, st) == hipSuccess &&
+                        hipEventSynchronize(e1) == hipSuccess &&
+                        hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+                total[t] += ms;
+            }
+        if (timed) {
+            int b = 0;
+            for (int t = 1; t < 3; ++t)
+                if (top[t] >= 0 && total[t] < total[b])
+                    b = t;
+            best = top[b];
         }
     }
     if (e0)
