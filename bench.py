@@ -228,10 +228,13 @@ def other_workload(name, dev):
                "bytes_model": "slice statistics 1R, slice gradient 1R+1W"}
     elif name == "head_kl":
         # the vocabulary head around the KL: two GEMMs of 2 ntok V hs flops
-        # each on the matrix cores, the KL rows and two conversions between
+        # each on the matrix cores, the KL rows and two conversions between.
+        # The whole batch is one chunk (15 GB of scratch): larger products
+        # run faster (chunks of 4096 rows: 13.7-14.0 ms a call; 8192: 12.8;
+        # 16384: 12.7).
         c = gi.head_inputs(16384, 151936, 1024, 256, 6001, dev, torch.bfloat16)
         ntok, hs = c["x"].shape
-        V, k, chunk, gscale = c["w"].shape[0], c["ids"].shape[1], 4096, 1024.0
+        V, k, chunk, gscale = c["w"].shape[0], c["ids"].shape[1], ntok, 1024.0
         dx = torch.empty((ntok, hs), device=dev)
         loss = torch.empty(ntok, device=dev)
         scratch = torch.empty(vl.vl_head_scratch_bytes(chunk, V, hs), dtype=torch.uint8,

@@ -222,19 +222,21 @@ def test_kl_bf16_sliced_full(vl):
     assert np.array_equal(d0.cpu().numpy().view(np.uint32), want.view(np.uint32))
 
 
-def test_head_kl_full(vl):
-    """Vocabulary head, 16384 x 151936 x 1024 bf16, k=256, chunks of 4096 (the
-    bench configuration): sampled rows, chunk edges included, against the
-    oracle on those rows (each row's loss and dx depend on that row alone).
-    Tolerances as in tests/test_gpu_head.py."""
+@pytest.mark.parametrize("chunk", [16384, 4096])
+def test_head_kl_full(vl, chunk):
+    """Vocabulary head, 16384 x 151936 x 1024 bf16, k=256, in one chunk of
+    16384 rows (the bench configuration) and in chunks of 4096: sampled rows,
+    chunk edges included, against the oracle on those rows (each row's loss
+    and dx depend on that row alone).  Tolerances as in
+    tests/test_gpu_head.py."""
     c = gi.head_inputs(16384, 151936, 1024, 256, 6001, DEV, torch.bfloat16)
     x, w, ids, probs = c["x"], c["w"], c["ids"], c["probs"]
     ntok, hs = x.shape
     V = w.shape[0]
     dx = torch.empty((ntok, hs), device=DEV)
     loss = torch.empty(ntok, device=DEV)
-    scratch = torch.empty(vl.vl_head_scratch_bytes(4096, V, hs), dtype=torch.uint8, device=DEV)
-    vl.vl_head_kl(x, w, ids, probs, dx, loss, ntok, 1024.0, 4096, scratch)
+    scratch = torch.empty(vl.vl_head_scratch_bytes(chunk, V, hs), dtype=torch.uint8, device=DEV)
+    vl.vl_head_kl(x, w, ids, probs, dx, loss, ntok, 1024.0, chunk, scratch)
     torch.cuda.synchronize()
     rows = sample(ntok, 12, 61, extra=(0, 4095, 4096, 8191, 12288, ntok - 1))
     xr = oracle.round_half(x[rows].cpu().numpy(), "bf16")
