@@ -124,8 +124,8 @@ def test_ce_tiny_config(vl):
     assert_ce(vl, c["logits"], c["labels"], c["rng"], c["scale"])
 
 
-CE_V = [1, 3, 8, 100, 511, 512, 1001, 2048, 2049, 4096, 8192, 8196, 32000, 32768, 32772,
-        65536, 65544, 100003]
+CE_V = [1, 3, 8, 100, 511, 512, 1001, 2048, 2049, 4096, 8192, 8196, 16384, 16388, 32000,
+        32768, 32772, 65536, 65544, 100003, 155648, 155656]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -201,10 +201,14 @@ def test_kl_multirow(vl, dtype, V):
 
 # ------------------------------------------------------------ KL
 
-# (20000, 1500): more teacher ids than threads in the 512-thread float32
-# block with the LDS prefetch, so threads handle several ids each.
-KL_VK = [(1, 1), (8, 3), (512, 16), (1001, 64), (2049, 5), (8192, 128), (32000, 64),
-         (20000, 1500), (32772, 200), (65544, 256), (131072, 2048), (151936, 256),
+# (20000, 1500): more teacher ids than threads in the 1024-thread float32
+# block with the LDS prefetch, so threads handle several ids each.  Either
+# side of each variant boundary: float32 16384 | 16388 (512 x 8 | 1024 x 8
+# with the LDS prefetch), 32768 | 32772 (staged | online); bf16 155648 |
+# 155656 (register refill | online).
+KL_VK = [(1, 1), (8, 3), (512, 16), (1001, 64), (2049, 5), (8192, 128), (16384, 64),
+         (16388, 64), (32000, 64), (20000, 1500), (32768, 100), (32772, 200), (65544, 256),
+         (131072, 2048), (151936, 256), (155648, 64), (155656, 64),
          (1 << 19, 64)]  # the largest KL vocabulary: two 64 KB bitmaps in LDS
 
 
