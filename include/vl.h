@@ -210,7 +210,10 @@ int vl_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream);
  * Cross-entropy over slices is the same calls with k = 1, ids = labels and
  * probs = 1.
  * Limits: 1 <= width, off + width <= 2^31 - 1, ld >= width, k >= 1,
- * nslice >= 1.  Ids outside every slice contribute nothing.
+ * nslice >= 1.  Ids outside every slice contribute nothing.  Slice rows are
+ * read as 16-byte vectors when the logits pointer is 16-byte aligned and
+ * ld and width times the element size are multiples of 16; otherwise one
+ * element at a time (same results, slower).
  */
 int vl_kl_slice_fwd(const void *logits, int dtype, int64_t ld, int64_t off, int64_t width,
                     const uint32_t *ids, const float *probs, int64_t k, float *part,
