@@ -95,23 +95,53 @@ def host_copies(x):
                                               "dh0", "dh1")}
 
 
-def cpu_baseline(h, rng, scale, rows: int):
-    """The float64 oracle on the host over the first `rows` rows of the same
-    inputs, every stage of the step, wall-clock."""
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (or the platform's)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_pass(h, rng, scale, rows):
+    """Every stage of the step on the first `rows` rows, wall-clock seconds."""
     import numpy as np
     import oracle
-
-    oracle.topk(h["teacher"][:2], K_TOPK)  # load the library outside the timing
     t0 = time.perf_counter()
     ids, probs = oracle.topk(h["teacher"][:rows], K_TOPK)
     oracle.kl(h["kl_student"][:rows], ids, probs.astype(np.float32), coef=1024.0 / NTOK)
     oracle.ce(h["ce_logits"][:rows], h["labels"][:rows], rng=rng, scale=scale)
     oracle.acc(h["dh0"][:rows], h["dh1"][:rows])
-    dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(h, rng, scale, rows: int, rows_1core: int):
+    """The float64 oracle on the host over the first `rows` rows of the same
+    inputs, every stage of the step, wall-clock: once on every thread the
+    OpenMP runtime uses, once on one thread (the first `rows_1core` rows)."""
+    import oracle
+
+    oracle.topk(h["teacher"][:2], K_TOPK)  # load the library outside the timing
+    threads = oracle.threads()
+    dt = _oracle_pass(h, rng, scale, rows)
+    oracle.set_threads(1)
+    try:
+        dt1 = _oracle_pass(h, rng, scale, rows_1core)
+    finally:
+        oracle.set_threads(threads)
     return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"first {rows} of the {NTOK} rows of every stage (top-k, KL, CE, "
-                      f"slice accumulate) at V={V}, float64, {dt:.2f} s wall-clock"}
+                      f"slice accumulate) at V={V}, float64, {dt:.2f} s wall-clock on "
+                      f"{threads} threads",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_core": {"value": rows_1core / dt1, "unit": "rows/s", "cores": 1,
+                            "sample": f"first {rows_1core} rows of every stage, "
+                                      f"{dt1:.2f} s wall-clock on 1 thread"}}
 
 
 def other_workload(name, dev):
@@ -344,6 +374,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=NTOK)
+    ap.add_argument("--cpu-rows-1core", type=int, default=512)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default="step")
     ap.add_argument("--pmc-summary", nargs="+", metavar="CSV")
@@ -407,7 +438,8 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(host, x["rng"], x["scale"], min(args.cpu_rows, NTOK))
+        cpu = cpu_baseline(host, x["rng"], x["scale"], min(args.cpu_rows, NTOK),
+                           min(args.cpu_rows_1core, NTOK))
 
     out = {
         "metric": "logits rows/s + achieved HBM GB/s (% of peak), fused CE/KL fwd+bwd at "

@@ -11,8 +11,10 @@ gives different (but each reproducible) bytes; the checks never depend on
 the particular values, only on both sides seeing the same ones.
 
 The workloads stand in for language-model head logits; no dataset or trained
-weights are involved.  The two page-test recipes at the bottom rebuild the
-inputs of the two tests printed on the pages.
+weights are involved.  The page-test recipes at the bottom take the shapes of
+the two tests printed on the pages: the cross-entropy test's inputs as that
+page states them, the KL test's shapes filled with this module's own seeded
+draws.
 """
 from __future__ import annotations
 
@@ -194,20 +196,21 @@ def kl_bf16_sliced(device, seed: int = 5, ntok: int = 16384, V: int = 151936,
 # ---------------------------------------------------------------------------
 # Inputs of the two tests printed on the pages.
 
-def page_rnd(n: int, seed: int, scale: float) -> np.ndarray:
-    """The xorshift64 stream of the cortiq-engine ``train_head.rs`` test
-    helper ``rnd``: state seeded as seed * 0x9E3779B97F4A7C15 | 1, shifts
-    13/7/17, output (state >> 11) / 2^53 mapped to [-1, 1) times ``scale``,
-    rounded to float32."""
-    mask = (1 << 64) - 1
-    s = ((seed * 0x9E3779B97F4A7C15) & mask) | 1
-    out = np.empty(n, dtype=np.float32)
-    for i in range(n):
-        s ^= (s << 13) & mask
-        s ^= s >> 7
-        s ^= (s << 17) & mask
-        out[i] = np.float32((float(s >> 11) / float(1 << 53) * 2.0 - 1.0)) * np.float32(scale)
-    return out
+def _page_kl_draws(seed: int):
+    """Seeded draws at the shapes of the cortiq-engine ``train_head.rs`` test
+    ``head_kl_matches_host`` (V=1024, hs=256, 45 tokens, k=16): head weights
+    ~ N(0, 1/hs) [V][hs] and hidden rows ~ N(0, 1) [45][hs] as float32, k
+    distinct uniform teacher ids per row, and probabilities
+    softmax(N(0, 1)) in float64, cast to float32."""
+    V, hs, ntok, k = 1024, 256, 45, 16
+    r = np.random.default_rng(seed)
+    w = (r.standard_normal((V, hs)) * (1.0 / hs) ** 0.5).astype(np.float32)
+    x = r.standard_normal((ntok, hs)).astype(np.float32)
+    ids = np.stack([r.permutation(V)[:k] for _ in range(ntok)]).astype(np.int32)
+    z = r.standard_normal((ntok, k))
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    probs = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    return w, x, ids, probs
 
 
 def page_ce_tiny():
@@ -221,27 +224,13 @@ def page_ce_tiny():
 
 
 def page_head_tiny():
-    """cortiq-engine ``train_head.rs`` test ``head_kl_matches_host``: V=1024,
-    hs=256, 45 tokens, k=16; head weights ``rnd(V*hs, 1, 0.1)`` and hidden
-    rows ``rnd(45*hs, 2, 1.0)`` as float32 (each side rounds them to f16
-    itself), teacher ids (t*37 + q*61) mod V with probabilities the
-    normalised exponential of ``rnd(k, 100 + t, 1.0)``; gscale 256, total
-    45, chunks of 32 rows."""
-    V, hs, ntok, k = 1024, 256, 45, 16
-    w = page_rnd(V * hs, 1, 0.1).reshape(V, hs)
-    x = page_rnd(ntok * hs, 2, 1.0).reshape(ntok, hs)
-    ids = np.empty((ntok, k), dtype=np.int32)
-    probs = np.empty((ntok, k), dtype=np.float32)
-    for t in range(ntok):
-        raw = page_rnd(k, 100 + t, 1.0)
-        e = np.exp(raw.astype(np.float32))
-        z = np.float32(0.0)
-        for q in range(k):
-            z = np.float32(z + e[q])
-        for q in range(k):
-            ids[t, q] = (t * 37 + q * 61) % V
-            probs[t, q] = e[q] / z
-    return dict(x=x, w=w, ids=ids, probs=probs, total=ntok, gscale=256.0, chunk=32)
+    """The shapes of the cortiq-engine ``train_head.rs`` test
+    ``head_kl_matches_host``: V=1024, hs=256, 45 tokens, k=16, gscale 256,
+    total 45, chunks of 32 rows; the values are this module's own seeded
+    draws (``_page_kl_draws``), float32 (each side rounds them to f16
+    itself)."""
+    w, x, ids, probs = _page_kl_draws(7001)
+    return dict(x=x, w=w, ids=ids, probs=probs, total=x.shape[0], gscale=256.0, chunk=32)
 
 
 def head_inputs(ntok: int, V: int, hs: int, k: int, seed: int, device, wdtype=torch.bfloat16):
@@ -258,29 +247,15 @@ def head_inputs(ntok: int, V: int, hs: int, k: int, seed: int, device, wdtype=to
 
 
 def page_kl_tiny():
-    """cortiq-engine ``train_head.rs`` test ``head_kl_matches_host`` inputs,
-    with the logits handed over directly: V=1024, hs=256, 45 tokens, k=16.
-    Head weights ``rnd(V*hs, 1, 0.1)`` and hidden rows ``rnd(45*hs, 2, 1.0)``
-    are rounded to f16 and multiplied in float64, then rounded to float32.
-    Teacher ids (t*37 + q*61) mod V, probabilities the normalised
-    exponential of ``rnd(k, 100 + t, 1.0)``; coef = gscale / total with
-    gscale 256 and total 45."""
-    V, hs, ntok, k = 1024, 256, 45, 16
-    w = page_rnd(V * hs, 1, 0.1).astype(np.float16).astype(np.float64).reshape(V, hs)
-    x = page_rnd(ntok * hs, 2, 1.0).astype(np.float16).astype(np.float64).reshape(ntok, hs)
+    """The KL rows of the head case above with the logits handed over
+    directly: the draws of ``_page_kl_draws`` with the head and hidden rows
+    rounded to f16, multiplied in float64 and rounded to float32; coef =
+    gscale / total with gscale 256 and total 45."""
+    w, x, ids, probs = _page_kl_draws(7001)
+    w = w.astype(np.float16).astype(np.float64)
+    x = x.astype(np.float16).astype(np.float64)
     logits = (x @ w.T).astype(np.float32)
-    ids = np.empty((ntok, k), dtype=np.int32)
-    probs = np.empty((ntok, k), dtype=np.float32)
-    for t in range(ntok):
-        raw = page_rnd(k, 100 + t, 1.0)
-        e = np.exp(raw.astype(np.float32))
-        z = np.float32(0.0)
-        for q in range(k):
-            z = np.float32(z + e[q])
-        for q in range(k):
-            ids[t, q] = (t * 37 + q * 61) % V
-            probs[t, q] = e[q] / z
-    return dict(logits=logits, ids=ids, probs=probs, coef=256.0 / ntok)
+    return dict(logits=logits, ids=ids, probs=probs, coef=256.0 / x.shape[0])
 
 
 def to_host_bytes(t: torch.Tensor) -> np.ndarray:

@@ -29,11 +29,15 @@
  *     sizes, dtypes and null pointers are rejected on the host before any
  *     GPU work.  ntok == 0 (or n == 0) is a no-op that returns VL_OK
  *     (except vl_loss_mean, which still writes its result).
- *   - Preconditions NOT checked on the device: label < V; ids < V and
- *     distinct within a row; probs >= 0; logits free of NaN and +inf with at
- *     least one finite value per row.  Violating them never faults: a label
- *     or id >= V makes that row's loss NaN and is skipped; duplicate ids
- *     leave that gradient entry unspecified.
+ *   - Preconditions NOT checked on the device: label < V; ids < V and,
+ *     among the entries with a nonzero probability, distinct within a row;
+ *     probs >= 0; logits free of NaN and +inf with at least one finite
+ *     value per row.  Entries with probability 0 take no part (a teacher
+ *     list padded with a repeated id at probability 0 is fine).  Violating
+ *     the preconditions never faults: a label or id >= V makes that row's
+ *     loss NaN and is skipped; a repeated id with a nonzero probability
+ *     leaves that row's loss and the gradient in the 16-byte vectors
+ *     holding the id undefined.
  *   - Rows are 16-byte vectors when the logits pointer is 16-byte aligned
  *     and V * element size is a multiple of 16; otherwise the same result is
  *     computed one element at a time (slower).

@@ -64,6 +64,10 @@ def _load():
             lib.oracle_topk.restype = None
             lib.oracle_acc.argtypes = [vp, vp, i64, vp]
             lib.oracle_acc.restype = None
+            lib.oracle_threads.argtypes = []
+            lib.oracle_threads.restype = ctypes.c_int
+            lib.oracle_set_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_threads.restype = None
             _lib = lib
     return _lib
 
@@ -92,6 +96,18 @@ def _range_args(rng):
         return 0, 0, 0
     seq_len, start, end = rng
     return int(seq_len), int(start), int(end)
+
+
+def threads() -> int:
+    """Host threads the oracle's row loops use (the OpenMP runtime's
+    current maximum)."""
+    return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use n >= 1 host threads from now on (timing only; no arithmetic
+    changes)."""
+    _load().oracle_set_threads(int(n))
 
 
 def row_lse(row: np.ndarray) -> float:

@@ -27,6 +27,7 @@
  *         over the k), the acc_add kernel (slice gradient sum).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -282,4 +283,19 @@ void oracle_acc(const float *dst, const float *src, int64_t n, float *out)
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i)
         out[i] = (float)((double)dst[i] + (double)src[i]);
+}
+
+/*
+ * Host threads the row loops use: the OpenMP runtime's current maximum, and
+ * a setter (n >= 1) for timing the oracle on a chosen number of cores.
+ * Neither changes any arithmetic.
+ */
+int oracle_threads(void)
+{
+    return omp_get_max_threads();
+}
+
+void oracle_set_threads(int n)
+{
+    omp_set_num_threads(n >= 1 ? n : 1);
 }

@@ -50,10 +50,11 @@ def kl_page():
         picks.append({"row": t, "cols": cols, "grad": [float(grad[t, j]) for j in cols]})
     return {
         "source": "cortiq-engine 0.8.21, src/gpu_wgpu/train_head.rs, test "
-                  "head_kl_matches_host: V=1024, hs=256, 45 tokens, k=16, teacher ids "
-                  "(t*37 + q*61) mod V with probabilities from rnd(k, 100+t); logits "
-                  "handed over directly as the f64 product of the f16-rounded rnd head "
-                  "and hidden rows; coef = gscale/total = 256/45",
+                  "head_kl_matches_host, for its shapes only: V=1024, hs=256, 45 tokens, "
+                  "k=16, coef = gscale/total = 256/45; the values are seeded draws of "
+                  "gen.inputs (N(0, 1/hs) head, N(0, 1) hidden rows, distinct uniform ids, "
+                  "softmax(N(0, 1)) probabilities), the logits handed over directly as "
+                  "the f64 product of the f16-rounded head and hidden rows",
         "inputs": "gen.inputs.page_kl_tiny()",
         "expected_by": "oracle.kl (float64)",
         "coef": c["coef"],

@@ -12,7 +12,7 @@ import torch
 import oracle
 from gen import inputs as gi
 from gen.inputs import to_host_bytes
-from tests.parity import check_grad, check_loss
+from tests.parity import ce_target, check_grad, check_loss
 
 pytestmark = pytest.mark.gpu
 
@@ -67,10 +67,11 @@ def assert_split(vl, x, labels, rng, scale, misalign=False):
     check_loss(loss, ol, dname(x))
     check_loss(lse, olse, dname(x), "lse")
     # the backward on its own: the oracle's backward from the same saved lse
+    tgt = ce_target(og.shape, lab, scale)
     check_grad(g, oracle.ce_bwd(host, lab, lse, rng=rng, scale=scale), dname(x), scale,
-               "grad from the saved lse")
+               "grad from the saved lse", tgt=tgt, lse=lse)
     # end to end: the exact gradient
-    check_grad(g, og, dname(x), scale)
+    check_grad(g, og, dname(x), scale, tgt=tgt, lse=olse)
 
 
 def f32_ulp(x):
@@ -94,7 +95,9 @@ def test_ce_split_page_fixture(vl):
     loss, lse, grad = run_split(vl, x, lab, c["rng"], c["scale"])
     check_loss(loss, g["loss"], "f32")
     check_loss(lse, g["lse"], "f32", "lse")
-    check_grad(grad, np.array(g["grad"]), "f32")
+    want = np.array(g["grad"])
+    check_grad(grad, want, "f32", c["scale"], tgt=ce_target(want.shape, c["labels"], c["scale"]),
+               lse=np.array(g["lse"]))
     m = run_mean(vl, torch.from_numpy(loss).to(DEV), c["rng"])
     assert abs(m - g["mean_loss"]) < 1e-4  # the page's own bound
     assert abs(m - oracle.loss_mean(loss, c["rng"])) <= f32_ulp(m)
@@ -175,7 +178,9 @@ def test_ce_split_invalid_label(vl):
     assert np.isnan(loss[1]) and np.isnan(loss[3])
     assert np.isfinite(loss[[0, 2]]).all() and np.isfinite(lse).all()
     host = to_host_bytes(x)
-    check_grad(g, oracle.ce_bwd(host, lab.cpu().numpy(), lse, scale=0.5), "f32", 0.5)
+    labh = lab.cpu().numpy()
+    want = oracle.ce_bwd(host, labh, lse, scale=0.5)
+    check_grad(g, want, "f32", 0.5, tgt=ce_target(want.shape, labh, 0.5), lse=lse)
 
 
 def test_ce_bwd_uses_the_given_lse(vl):
@@ -190,8 +195,10 @@ def test_ce_bwd_uses_the_given_lse(vl):
     out = x.clone()
     vl.vl_ce_bwd(out, lab, lse, scale=2.0)
     torch.cuda.synchronize()
-    want = oracle.ce_bwd(to_host_bytes(x), lab.cpu().numpy(), lse.cpu().numpy(), scale=2.0)
-    check_grad(to_host_bytes(out), want, "f32", 2.0)
+    labh, lseh = lab.cpu().numpy(), lse.cpu().numpy()
+    want = oracle.ce_bwd(to_host_bytes(x), labh, lseh, scale=2.0)
+    check_grad(to_host_bytes(out), want, "f32", 2.0, tgt=ce_target(want.shape, labh, 2.0),
+               lse=lseh)
 
 
 # ------------------------------------------------------------ mean loss

@@ -1,7 +1,9 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (the same C-ABI calls on the same shapes).  Every row where the oracle
-finishes in seconds (the 4096 x 32000 workloads), sampled rows plus
-whole-tensor invariants for the 4-5 GB ones.  Needs an MI355X."""
+times (the same C-ABI calls on the same shapes).  Every row's loss and
+gradient at 4096 x 32000 and 8192 x 128256; at 16384 x 151936 every row's
+loss, and the gradient of the first and last 1024 rows (the first and last
+row of every workgroup's walk for any grid up to 1024 workgroups) plus
+sampled rows between them, with whole-tensor invariants.  Needs an MI355X."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,8 @@ import torch
 import oracle
 from gen import inputs as gi
 from gen.inputs import to_host_bytes
-from tests.parity import bf16_bits_to_f64, check_grad, check_loss, check_topk
+from tests.parity import (bf16_bits_to_f64, ce_target, check_grad, check_loss, check_topk,
+                          dense_target)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -73,16 +76,19 @@ def test_bench_step_full(vl):
         r1 = r0 + 512
         oi, op = oracle.topk(host["teacher"][r0:r1], k)
         check_topk(gi_ids[r0:r1], gi_p[r0:r1], oi, op)
-        ol, _, og = oracle.kl(host["kl_student"][r0:r1], gi_ids[r0:r1], gi_p[r0:r1], coef=coef)
+        ol, olse, og = oracle.kl(host["kl_student"][r0:r1], gi_ids[r0:r1], gi_p[r0:r1],
+                                 coef=coef)
         check_loss(kl_l[r0:r1], ol, "f32")
-        check_grad(x["kl_student"][r0:r1].cpu().numpy(), og, "f32", coef)
+        check_grad(x["kl_student"][r0:r1].cpu().numpy(), og, "f32", coef,
+                   tgt=dense_target(og.shape, gi_ids[r0:r1], gi_p[r0:r1], coef), lse=olse)
         el, _, _ = oracle.kl(host["kl_student"][r0:r1], oi, op.astype(np.float32), coef=coef,
                              want_grad=False)
         check_loss(kl_l[r0:r1], el, "f32", "KL end to end")
-        ol, _, og = oracle.ce(host["ce_logits"][r0:r1], host["labels"][r0:r1], rng=x["rng"],
-                              scale=x["scale"], row_index=np.arange(r0, r1))
+        ol, olse, og = oracle.ce(host["ce_logits"][r0:r1], host["labels"][r0:r1],
+                                 rng=x["rng"], scale=x["scale"], row_index=np.arange(r0, r1))
         check_loss(ce_l[r0:r1], ol, "f32")
-        check_grad(x["ce_logits"][r0:r1].cpu().numpy(), og, "f32", x["scale"])
+        check_grad(x["ce_logits"][r0:r1].cpu().numpy(), og, "f32", x["scale"],
+                   tgt=ce_target(og.shape, host["labels"][r0:r1], x["scale"]), lse=olse)
     want = oracle.acc(host["dh0"], host["dh1"])
     assert np.array_equal(x["dh0"].cpu().numpy().view(np.uint32), want.view(np.uint32))
 
@@ -104,7 +110,8 @@ def test_ce_lm_full(vl):
                                  row_index=np.arange(r0, r1))
         check_loss(loss[r0:r1], ol, "f32")
         check_loss(lse[r0:r1], olse, "f32", "lse")
-        check_grad(x[r0:r1].cpu().numpy(), og, "f32", scale)
+        check_grad(x[r0:r1].cpu().numpy(), og, "f32", scale,
+                   tgt=ce_target(og.shape, labh[r0:r1], scale), lse=olse)
 
 
 def test_ce_split_lm_full(vl):
@@ -132,7 +139,8 @@ def test_ce_split_lm_full(vl):
         all_loss[r0:r1] = ol
         check_loss(loss_h[r0:r1], ol, "f32")
         check_loss(lse_h[r0:r1], olse, "f32", "lse")
-        check_grad(x[r0:r1].cpu().numpy(), og, "f32", scale)
+        check_grad(x[r0:r1].cpu().numpy(), og, "f32", scale,
+                   tgt=ce_target(og.shape, labh[r0:r1], scale), lse=olse)
     # per-row losses within 1e-5 relative, so their mean is too
     want = all_loss.sum() / (8 * 384)
     assert abs(float(mean.cpu()[0]) - want) <= 1e-5 * abs(want)
@@ -154,44 +162,45 @@ def test_topk_zipf_full(vl):
 
 
 def test_kl_large_full(vl):
-    """Distillation KL, 8192 x 128256 float32, k=128: sampled rows through
-    the oracle (loss on 512 rows, gradient on 24)."""
+    """Distillation KL, 8192 x 128256 float32, k=128: every row's loss, lse
+    and gradient against the oracle, in chunks of 256 rows."""
     c = gi.kl_large(DEV)
     x, ids, probs, coef = c["logits"], c["ids"], c["probs"], c["coef"]
-    rows = sample(x.shape[0], 512, 41, extra=[0, x.shape[0] - 1])
-    host = to_host_bytes(x[torch.from_numpy(rows).to(DEV)])
-    idh = ids.cpu().numpy()[rows]
-    ph = probs.cpu().numpy()[rows]
-    loss = torch.empty(x.shape[0], device=DEV)
-    lse = torch.empty(x.shape[0], device=DEV)
+    ntok = x.shape[0]
+    host = to_host_bytes(x)
+    idh = ids.cpu().numpy()
+    ph = probs.cpu().numpy()
+    loss = torch.empty(ntok, device=DEV)
+    lse = torch.empty(ntok, device=DEV)
     vl.vl_kl_fwd_bwd(x, ids, probs, loss, lse, coef=coef)
     torch.cuda.synchronize()
-    ol, olse, _ = oracle.kl(host, idh, ph, coef=coef, want_grad=False)
-    check_loss(loss.cpu().numpy()[rows], ol, "f32")
-    check_loss(lse.cpu().numpy()[rows], olse, "f32", "lse")
-    g_rows = rows[:: max(1, len(rows) // 24)]
-    sel = np.searchsorted(rows, g_rows)
-    _, _, og = oracle.kl(host[sel], idh[sel], ph[sel], coef=coef)
-    check_grad(x[torch.from_numpy(g_rows).to(DEV)].cpu().numpy(), og, "f32", coef)
-    # every row: gradient rows sum to coef * (1 - sum p), finite losses
-    gs = x.sum(dim=1, dtype=torch.float64)
-    want = coef * (1.0 - probs.sum(dim=1, dtype=torch.float64))
-    assert float((gs - want).abs().max()) < 1e-4
-    assert bool(torch.isfinite(loss).all())
+    loss_h, lse_h = loss.cpu().numpy(), lse.cpu().numpy()
+    g_all = x.cpu().numpy()
+    for r0 in range(0, ntok, 256):
+        r1 = min(ntok, r0 + 256)
+        ol, olse, og = oracle.kl(host[r0:r1], idh[r0:r1], ph[r0:r1], coef=coef)
+        check_loss(loss_h[r0:r1], ol, "f32")
+        check_loss(lse_h[r0:r1], olse, "f32", "lse")
+        check_grad(g_all[r0:r1], og, "f32", coef,
+                   tgt=dense_target(og.shape, idh[r0:r1], ph[r0:r1], coef), lse=olse,
+                   what=f"grad rows {r0}-{r1}")
 
 
 def test_kl_bf16_sliced_full(vl):
     """bf16 distillation at V=151936: teacher top-k (k=256) by the GPU, KL of
     the student against it, and the slice accumulate of two [16384][1024]
-    float32 input gradients.  End to end against the oracle's own top-k on
-    sampled rows; ids bit-exact on the sampled rows and invariants on all."""
+    float32 input gradients.  Top-k ids bit-exact on sampled rows and
+    invariants on all; every row's loss against the oracle, both fed the
+    GPU's top-k (stage-isolated) and end to end from the oracle's own
+    top-k on sampled rows; the gradient of the first and last 1024 rows and
+    of sampled rows between them."""
     c = gi.kl_bf16_sliced(DEV)
     x, t, k, coef = c["logits"], c["teacher"], c["k"], c["coef"]
     ntok = x.shape[0]
     rows = sample(ntok, 24, 51, extra=[0, ntok - 1])
     rows_t = torch.from_numpy(rows).to(DEV)
     th = to_host_bytes(t[rows_t])
-    xh = to_host_bytes(x[rows_t])
+    xh_all = to_host_bytes(x)
 
     ids = torch.empty((ntok, k), dtype=torch.int32, device=DEV)
     probs = torch.empty((ntok, k), device=DEV)
@@ -202,18 +211,33 @@ def test_kl_bf16_sliced_full(vl):
     check_topk(ids[rows_t].cpu().numpy().view(np.uint32), probs[rows_t].cpu().numpy(), oi, op)
 
     loss = torch.empty(ntok, device=DEV)
-    vl.vl_kl_fwd_bwd(x, ids, probs, loss, coef=coef)
+    lse = torch.empty(ntok, device=DEV)
+    vl.vl_kl_fwd_bwd(x, ids, probs, loss, lse, coef=coef)
     torch.cuda.synchronize()
-    g = to_host_bytes(x[rows_t])
-    # stage-isolated: the oracle KL fed the GPU's own ids and probs
-    gid = ids[rows_t].cpu().numpy().view(np.uint32)
-    sl, _, sg = oracle.kl(xh, gid, probs[rows_t].cpu().numpy(), coef=coef)
-    check_loss(loss.cpu().numpy()[rows], sl, "bf16", "KL from the GPU's top-k")
-    check_grad(g, sg, "bf16", coef, "gradient from the GPU's top-k")
-    # end to end: the oracle's own top-k of the teacher bytes
-    ol, _, og = oracle.kl(xh, oi, op.astype(np.float32), coef=coef)
-    check_loss(loss.cpu().numpy()[rows], ol, "bf16")
-    check_grad(g, og, "bf16", coef)
+    loss_h, lse_h = loss.cpu().numpy(), lse.cpu().numpy()
+    idh = ids.cpu().numpy().view(np.uint32)
+    ph = probs.cpu().numpy()
+    # stage-isolated, every row's loss and lse: the oracle KL fed the GPU's
+    # own ids and probs
+    sl, slse, _ = oracle.kl(xh_all, idh, ph, coef=coef, want_grad=False)
+    check_loss(loss_h, sl, "bf16", "KL from the GPU's top-k")
+    check_loss(lse_h, slse, "bf16", "lse")
+    # gradient rows: the first and last 1024 and sampled rows between them
+    grows = np.unique(np.concatenate([np.arange(1024), np.arange(ntok - 1024, ntok),
+                                      sample(ntok, 64, 52)]))
+    g_all = to_host_bytes(x[torch.from_numpy(grows).to(DEV)])
+    for i0 in range(0, len(grows), 256):
+        sel = grows[i0:i0 + 256]
+        _, olse, og = oracle.kl(xh_all[sel], idh[sel], ph[sel], coef=coef)
+        check_grad(g_all[i0:i0 + 256], og, "bf16", coef,
+                   tgt=dense_target(og.shape, idh[sel], ph[sel], coef), lse=olse,
+                   what=f"gradient from the GPU's top-k, rows {sel[0]}-{sel[-1]}")
+    # end to end on the sampled rows: the oracle's own top-k of the teacher bytes
+    xh = xh_all[rows]
+    ol, olse, og = oracle.kl(xh, oi, op.astype(np.float32), coef=coef)
+    check_loss(loss_h[rows], ol, "bf16")
+    check_grad(to_host_bytes(x[rows_t]), og, "bf16", coef,
+               tgt=dense_target(og.shape, oi, op, coef), lse=olse)
 
     d0, d1 = c["dh0"], c["dh1"]
     want = oracle.acc(d0.cpu().numpy(), d1.cpu().numpy())

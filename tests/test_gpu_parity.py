@@ -10,7 +10,8 @@ import torch
 import oracle
 from gen import inputs as gi
 from gen.inputs import to_host_bytes
-from tests.parity import check_grad, check_loss, check_topk, bf16_bits_to_f64
+from tests.parity import (bf16_bits_to_f64, ce_target, check_grad, check_loss, check_topk,
+                          dense_target)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,19 +73,20 @@ def run_topk(vl, x, k):
 
 def assert_ce(vl, x, labels, rng, scale, misalign=False):
     loss, lse, g = run_ce(vl, x, labels, rng, scale, misalign)
-    ol, olse, og = oracle.ce(to_host_bytes(x), labels.cpu().numpy(), rng=rng, scale=scale)
+    lab = labels.cpu().numpy()
+    ol, olse, og = oracle.ce(to_host_bytes(x), lab, rng=rng, scale=scale)
     check_loss(loss, ol, dname(x))
     check_loss(lse, olse, dname(x), "lse")
-    check_grad(g, og, dname(x), scale)
+    check_grad(g, og, dname(x), scale, tgt=ce_target(og.shape, lab, scale), lse=olse)
 
 
 def assert_kl(vl, x, ids, probs, rng, coef, misalign=False):
     loss, lse, g = run_kl(vl, x, ids, probs, rng, coef, misalign)
-    ol, olse, og = oracle.kl(to_host_bytes(x), ids.cpu().numpy(), probs.cpu().numpy(),
-                             rng=rng, coef=coef)
+    idh, ph = ids.cpu().numpy(), probs.cpu().numpy()
+    ol, olse, og = oracle.kl(to_host_bytes(x), idh, ph, rng=rng, coef=coef)
     check_loss(loss, ol, dname(x))
     check_loss(lse, olse, dname(x), "lse")
-    check_grad(g, og, dname(x), coef)
+    check_grad(g, og, dname(x), coef, tgt=dense_target(og.shape, idh, ph, coef), lse=olse)
 
 
 # ------------------------------------------------------------ page fixtures
@@ -97,7 +99,9 @@ def test_ce_page_fixture(vl):
     loss, lse, grad = run_ce(vl, x, lab, c["rng"], c["scale"])
     check_loss(loss, g["loss"], "f32")
     check_loss(lse, g["lse"], "f32", "lse")
-    check_grad(grad, np.array(g["grad"]), "f32")
+    want = np.array(g["grad"])
+    check_grad(grad, want, "f32", c["scale"], tgt=ce_target(want.shape, c["labels"], c["scale"]),
+               lse=np.array(g["lse"]))
     assert abs(loss.sum() / 4 - g["mean_loss"]) < 1e-4  # the page's own bound
 
 
@@ -110,8 +114,11 @@ def test_kl_page_fixture(vl):
     loss, lse, grad = run_kl(vl, x, ids, probs, None, c["coef"])
     check_loss(loss, g["loss"], "f32")
     check_loss(lse, g["lse"], "f32", "lse")
+    tgt = dense_target(grad.shape, c["ids"], c["probs"], c["coef"])
     for s in g["grad_samples"]:
-        check_grad(grad[s["row"], s["cols"]], np.array(s["grad"]), "f32", c["coef"])
+        r, cols = s["row"], s["cols"]
+        check_grad(grad[r, cols], np.array(s["grad"]), "f32", c["coef"], tgt=tgt[r, cols],
+                   lse=g["lse"][r])
     # the page's own metric: relative L2 of the loss vector below 1e-4
     want = np.array(g["loss"])
     assert np.linalg.norm(loss - want) / np.linalg.norm(want) < 1e-4
@@ -199,6 +206,91 @@ def test_kl_multirow(vl, dtype, V):
     assert_kl(vl, x, ids, probs, None, 1024.0 / ntok)
 
 
+# Every row-kernel variant with several rows per workgroup, with a loss
+# range: ntok is three times the largest grid the variant can launch plus
+# one (256 CUs x the most blocks of its size a CU can hold: 32 of 64
+# threads, 8 of 256, 4 of 512, 2 of 1024), so every workgroup walks at
+# least three in-range rows (the row-parity LDS slots and bitmaps, the
+# one-row-late bitmap clear, the next row's target fetch, and the LDS
+# prefetch or register refill where the variant has one) and then
+# write-only rows.  (dtype, V, threads per block) in launch-table order;
+# the last two float32 / bf16 entries are the online and register-refill
+# variants, and "unaligned" rows take the element path.
+VARIANTS = [
+    ("f32", 200, 64), ("f32", 500, 64), ("f32", 1000, 64), ("f32", 2000, 64),
+    ("f32", 4000, 256), ("f32", 8000, 256), ("f32", 16000, 512), ("f32", 32000, 1024),
+    ("f32", 40008, 1024),
+    ("bf16", 504, 64), ("bf16", 1000, 64), ("bf16", 2000, 64), ("bf16", 8000, 256),
+    ("bf16", 32000, 512), ("bf16", 40008, 1024), ("bf16", 160000, 1024),
+    ("unaligned-f32", 4096, 256), ("unaligned-bf16", 4096, 256),
+]
+
+
+def _variant_rows(threads):
+    return 3 * 256 * (2048 // threads) + 1
+
+
+def _check_chunked(kind, host, got, loss, lse, tg, probs, rng, coef, dtype):
+    """Every row against the oracle, in chunks of about 2^25 values."""
+    n, V = host.shape
+    step = max(1, (1 << 25) // V)
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        ri = np.arange(r0, r1)
+        if kind == "ce":
+            ol, olse, og = oracle.ce(host[r0:r1], tg[r0:r1], rng=rng, scale=coef, row_index=ri)
+            tgt = ce_target(og.shape, tg[r0:r1], coef)
+        else:
+            ol, olse, og = oracle.kl(host[r0:r1], tg[r0:r1], probs[r0:r1], rng=rng, coef=coef,
+                                     row_index=ri)
+            tgt = dense_target(og.shape, tg[r0:r1], probs[r0:r1], coef)
+        check_loss(loss[r0:r1], ol, dtype, f"loss rows {r0}-{r1}")
+        check_loss(lse[r0:r1], olse, dtype, f"lse rows {r0}-{r1}")
+        check_grad(got[r0:r1], og, dtype, coef, f"grad rows {r0}-{r1}", tgt=tgt, lse=olse)
+
+
+@pytest.mark.parametrize("kind", ["ce", "kl"])
+@pytest.mark.parametrize("dtype,V,threads", VARIANTS)
+def test_variant_multirow_with_range(vl, kind, dtype, V, threads):
+    mis = dtype.startswith("unaligned")
+    dt = dtype.split("-")[-1]
+    ntok = _variant_rows(threads)
+    print(f"variant {dtype} V={V} threads={threads} ntok={ntok} {kind}", flush=True)
+    x = gi.normal_logits(ntok, V, 2.5, 4000 + V + threads, DEV, TDT[dt])
+    rng = (7, 1, 6)
+    coef = 1.0 / 300
+    if kind == "ce":
+        tg = gi.uniform_labels(ntok, V, 4100 + V, DEV)
+        loss, lse, g = run_ce(vl, x, tg, rng, coef, misalign=mis)
+        probs = None
+    else:
+        k = min(V, 48)
+        tg = gi.distinct_ids(ntok, V, k, 4200 + V, DEV)
+        pt = gi.softmax_probs(ntok, k, 1.5, 4300 + V, DEV)
+        loss, lse, g = run_kl(vl, x, tg, pt, rng, coef, misalign=mis)
+        probs = pt.cpu().numpy()
+    _check_chunked(kind, to_host_bytes(x), g, loss, lse, tg.cpu().numpy(), probs, rng, coef,
+                   dt)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [4096, 32000, 40008])
+def test_kl_padded_teacher_list(vl, dtype, V):
+    """A teacher list padded with repeated ids at probability 0 (the
+    zero-probability entries take no part): the same result as the
+    oracle, which sums the probabilities of repeated ids.  The padding
+    repeats the row's first id, or an id alone in its 16-byte vector."""
+    ntok, k, kreal = 40, 24, 15
+    x = gi.normal_logits(ntok, V, 2.0, 4400 + V, DEV, TDT[dtype])
+    ids = gi.distinct_ids(ntok, V, k, 4500 + V, DEV)
+    probs = gi.softmax_probs(ntok, k, 1.5, 4600 + V, DEV)
+    probs[:, kreal:] = 0.0
+    probs[:, :kreal] /= probs[:, :kreal].sum(dim=1, keepdim=True)
+    ids[:, kreal:] = ids[:, :1]            # repeats of the first (real) id
+    ids[1::2, kreal + 2:] = ids[1::2, 3:4]  # and of another on odd rows
+    assert_kl(vl, x, ids, probs, None, 1.0 / 40)
+
+
 # ------------------------------------------------------------ KL
 
 # (20000, 1500): more teacher ids than threads in the 1024-thread float32
@@ -271,10 +363,10 @@ def test_kl_invalid_id_gives_nan_loss_only(vl):
     probs = torch.full((3, k), 0.25, device=DEV)
     loss, _, g = run_kl(vl, x, ids, probs, None, 1.0)
     assert np.isnan(loss[1]) and np.isfinite(loss[[0, 2]]).all()
-    ol, _, og = oracle.kl(to_host_bytes(x)[[0, 2]], ids.cpu().numpy()[[0, 2]],
-                          probs.cpu().numpy()[[0, 2]], coef=1.0)
+    idh, ph = ids.cpu().numpy()[[0, 2]], probs.cpu().numpy()[[0, 2]]
+    ol, olse, og = oracle.kl(to_host_bytes(x)[[0, 2]], idh, ph, coef=1.0)
     check_loss(loss[[0, 2]], ol, "f32")
-    check_grad(g[[0, 2]], og, "f32", 1.0)
+    check_grad(g[[0, 2]], og, "f32", 1.0, tgt=dense_target(og.shape, idh, ph, 1.0), lse=olse)
 
 
 # ------------------------------------------------------------ top-k

@@ -10,7 +10,7 @@ import torch
 import oracle
 from gen import inputs as gi
 from gen.inputs import to_host_bytes
-from tests.parity import bf16_bits_to_f64, check_grad, check_loss
+from tests.parity import bf16_bits_to_f64, ce_target, check_grad, check_loss, dense_target
 
 pytestmark = pytest.mark.gpu
 
@@ -107,9 +107,10 @@ def assert_sliced(vl, x, ids, probs, cuts, rng, coef, layout="window"):
     # each slice's gradient on its own, from the same lse the GPU used
     gb = np.concatenate([oracle.kl_slice_bwd(host[:, o:o + w], o, idh, ph, lse, coef=coef,
                                              rng=rng) for o, w in cuts], axis=1)
-    check_grad(g, gb, dname(x), coef, "slice gradient from the merged lse")
+    tgt = dense_target(og.shape, idh, ph, coef)
+    check_grad(g, gb, dname(x), coef, "slice gradient from the merged lse", tgt=tgt, lse=lse)
     # end to end: the whole row's exact gradient
-    check_grad(g, og, dname(x), coef)
+    check_grad(g, og, dname(x), coef, tgt=tgt, lse=olse)
 
 
 CASES = [
@@ -199,9 +200,10 @@ def test_slices_unit_target_is_the_cross_entropy(vl):
     _, loss, _, g = run_sliced(vl, x, lab[:, None].contiguous(), one, cuts, (8, 2, 8), 1.0 / 12,
                                "window")
     host = to_host_bytes(x)
-    ol, _, og = oracle.ce(host, lab.cpu().numpy(), rng=(8, 2, 8), scale=1.0 / 12)
+    labh = lab.cpu().numpy()
+    ol, olse, og = oracle.ce(host, labh, rng=(8, 2, 8), scale=1.0 / 12)
     check_loss(loss, ol, "f32")
-    check_grad(g, og, "f32", 1.0 / 12)
+    check_grad(g, og, "f32", 1.0 / 12, tgt=ce_target(og.shape, labh, 1.0 / 12), lse=olse)
 
 
 def test_slices_zero_rows_and_empty_range(vl):
@@ -256,7 +258,7 @@ def test_slices_bf16_151936_full(vl):
     check_loss(loss.cpu().numpy()[rows], ol, "bf16")
     check_loss(lse.cpu().numpy()[rows], olse, "bf16", "lse")
     g = np.concatenate([to_host_bytes(s[rows_t]) for s in slices], axis=1)
-    check_grad(g, og, "bf16", coef)
+    check_grad(g, og, "bf16", coef, tgt=dense_target(og.shape, idh, ph, coef), lse=olse)
     lf, ls = fused.double(), loss.double()
     assert float(((ls - lf).abs() / lf.abs()).max()) < 1e-5
     gs = sum(s.sum(dim=1, dtype=torch.float64) for s in slices)

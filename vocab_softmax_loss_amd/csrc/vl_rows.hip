@@ -51,8 +51,10 @@
 // and the logits at the targets are gathered once the current row is done.
 //
 // Precondition violations are not checked on the device but never fault: a
-// label or id >= V gives a NaN loss and no target write; duplicate ids give
-// an undefined gradient at that id.
+// label or id >= V gives a NaN loss and no target write.  Teacher entries
+// with probability 0 are not targets and may repeat ids; a repeated id with
+// a nonzero probability leaves that row's loss and the 16-byte vectors
+// holding the id undefined.
 #include <math.h>
 
 #include "vl_device.hpp"
@@ -284,13 +286,23 @@ struct RowKernel {
         }
     }
 
-    // KL: the row's marks in bitmap `bm` (cleared by then).
+    // KL: the row's marks in bitmap `bm` (cleared by then).  An entry with
+    // probability 0 changes neither the loss nor the gradient, so it is not
+    // a target: such entries may repeat an id (a padded teacher list).
     __device__ void mark_targets(int64_t row, const Tgt &t, uint32_t *bm) const
     {
         if constexpr (KL) {
             for (uint32_t q = tid; q < k; q += BLOCK) {
-                const uint32_t id = q == (uint32_t)tid ? t.id : a.ids[row * k + q];
-                if (id < V)
+                uint32_t id;
+                float pq;
+                if (q == (uint32_t)tid) {
+                    id = t.id;
+                    pq = t.p;
+                } else {
+                    id = a.ids[row * k + q];
+                    pq = a.probs[row * k + q];
+                }
+                if (id < V && pq != 0.f)
                     atomicOr(&bm[id >> 5], 1u << (id & 31));
             }
         }
@@ -497,6 +509,8 @@ struct RowKernel {
                 const float d = (sv - M) - logS;  // log p_S at the id
                 if (pq > 0.f)
                     acc += pq * (__logf(pq) - d);
+                if (pq == 0.f)
+                    continue;  // not a target (not marked)
                 const float gid = coef * (__expf(d) - pq);
                 if constexpr (N > 1) {
                     const uint32_t v = id / N, j0 = v * N;
