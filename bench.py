@@ -18,8 +18,8 @@ Prints one JSON line.  `value` is logits rows per second of the whole step;
 the launch stream around every launch of the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-                    [--workload step|ce_lm|ce_split|topk_zipf|kl_large|kl_bf16|kl_sliced|head_kl|
-                                copy_calib]
+                    [--workload step|ce_lm|ce_split|topk_zipf|kl_large|kl_large_unsplit|kl_bf16|
+                                kl_sliced|head_kl|copy_calib]
     python bench.py --pmc-summary <counter_collection.csv> ...
 
 The other workloads time one configuration each at its full size, for
@@ -187,19 +187,29 @@ def other_workload(name, dev):
         calls = [("topk", lambda: vl.vl_topk_renorm(t, k, ids, probs))]
         nbytes = {"topk": ntok * V * 4 + ntok * k * 8}
         cfg = {"workload": gi.TOPK_ZIPF.name, "ntok": ntok, "V": V, "k": k, "dtype": "f32"}
-    elif name == "kl_large":
+    elif name in ("kl_large", "kl_large_unsplit"):
         c = gi.kl_large(dev)
         x = c["logits"]
         ntok, V = x.shape
         k = c["ids"].shape[1]
         loss = torch.empty(ntok, device=dev)
-        calls = [("kl", lambda: vl.vl_kl_fwd_bwd(x, c["ids"], c["probs"], loss, coef=c["coef"]))]
-        # algorithmic bytes: each row read once and written once.  The row
-        # does not fit on one CU, so the kernel reads about a quarter of it
-        # a second time (the rest of pass 2 comes from registers and LDS).
+        if name == "kl_large":
+            # the workspace call: each 128256-value row split over four
+            # co-resident workgroups, read once and written once
+            ws = torch.empty(vl.vl_split_workspace_bytes(), dtype=torch.uint8, device=dev)
+            calls = [("kl", lambda: vl.vl_kl_fwd_bwd_ws(x, c["ids"], c["probs"], loss, ws,
+                                                        coef=c["coef"]))]
+            model = "1R+1W (rows split over 4 workgroups)"
+        else:
+            # one workgroup per row: the row does not fit one CU, so the
+            # kernel reads about a quarter of it a second time (the rest of
+            # pass 2 comes from registers and LDS)
+            calls = [("kl", lambda: vl.vl_kl_fwd_bwd(x, c["ids"], c["probs"], loss,
+                                                     coef=c["coef"]))]
+            model = "1R+1W algorithmic (the kernel re-reads ~27% of each row)"
         nbytes = {"kl": ntok * 2 * V * 4 + ntok * k * 8 + ntok * 4}
         cfg = {"workload": gi.KL_LARGE.name, "ntok": ntok, "V": V, "k": k, "dtype": "f32",
-               "bytes_model": "1R+1W (the kernel re-reads ~27% of each row)"}
+               "bytes_model": model}
     elif name == "kl_bf16":
         c = gi.kl_bf16_sliced(dev)
         x, t, k = c["logits"], c["teacher"], c["k"]

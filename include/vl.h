@@ -155,6 +155,48 @@ int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *pro
                   float coef, hipStream_t stream);
 
 /*
+ * Workspace bytes the two calls below need at least (256 KiB).
+ */
+size_t vl_split_workspace_bytes(void);
+
+/*
+ * vl_ce_fwd_bwd_ws / vl_kl_fwd_bwd_ws -- vl_ce_fwd_bwd and vl_kl_fwd_bwd
+ * with a workspace that lets a row too long for one compute unit's
+ * registers be split over 2, 4 or 8 co-resident workgroups [KL: Head, the
+ * vocabulary cut into column slices; module doc and kl_rows for the loss
+ * and gradient; CE: module doc, backward].  Each workgroup holds one column
+ * part of the row in registers; the parts swap their statistics (max, sum
+ * of exp, teacher mass and teacher term, 16 bytes) through the workspace,
+ * every part forms the row's logsumexp from all of them and writes its part
+ * of the gradient from registers, so the row is read once and written once.
+ * The split takes rows whose logits pointer is 16-byte aligned with V a
+ * multiple of 4 (float32) or 8 (bf16), float32 V in (32768, 524288] and bf16
+ * V in (155648, 458752] (the KL's own limit V <= 2^19 still applies); other
+ * rows run the kernels of vl_ce_fwd_bwd / vl_kl_fwd_bwd (a bf16 row of up to
+ * 155648 values already fits one workgroup's registers) and leave the
+ * workspace unused.
+ *   workspace        device buffer of at least vl_split_workspace_bytes()
+ *                    bytes, owned by the caller; its contents on entry do
+ *                    not matter (the call clears what it uses, on `stream`,
+ *                    before it starts).  Calls that share a workspace must
+ *                    not run at the same time; calls in order on one stream
+ *                    may share one.
+ *   workspace_bytes  its size.
+ * Other arguments, results and limits: as vl_ce_fwd_bwd / vl_kl_fwd_bwd.
+ * Losses, lse and gradients agree with theirs within rounding (the row's
+ * sums are taken in another order).  The split runs as one cooperative
+ * launch, so all its workgroups are resident together; should a part's
+ * partners still fail to answer within about a second, that row's loss,
+ * lse and gradient come out NaN and the call completes.
+ */
+int vl_ce_fwd_bwd_ws(void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
+                     int64_t ntok, int64_t V, const vl_range *rng, float scale, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+int vl_kl_fwd_bwd_ws(void *logits, int dtype, const uint32_t *ids, const float *probs, int64_t k,
+                     float *loss, float *lse, int64_t ntok, int64_t V, const vl_range *rng,
+                     float coef, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Teacher top-k with renormalised probabilities [KL: topk_rows].
  *   logits  [ntok][V] dtype, read only.
  *   ids     [ntok][k] uint32, written: the k ids first in the order (value

@@ -25,11 +25,12 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(vl_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_thirteen_calls():
+def test_header_declares_the_calls():
     assert declared_functions() == sorted(
         ["vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
          "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
-         "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror"])
+         "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror",
+         "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -241,3 +242,44 @@ def test_slice_merge_host_checks(lib):
     assert f(P16, 2, None, None, 4, None, None) == VL_EINVAL
     assert f(P16, 2, P, None, 4, rng(0, 0, 0), None) == VL_EINVAL
     assert f(None, 2, None, None, 0, None, None) == VL_OK
+
+
+def ce_ws(lib, **kw):
+    a = dict(logits=P, dtype=0, labels=P, loss=P, lse=None, ntok=4, V=10, rng=None,
+             scale=1.0, ws=P, ws_bytes=lib.vl_split_workspace_bytes(), stream=None)
+    a.update(kw)
+    return lib.vl_ce_fwd_bwd_ws(a["logits"], a["dtype"], a["labels"], a["loss"], a["lse"],
+                                a["ntok"], a["V"], a["rng"], a["scale"], a["ws"],
+                                a["ws_bytes"], a["stream"])
+
+
+def kl_ws(lib, **kw):
+    a = dict(logits=P, dtype=0, ids=P, probs=P, k=2, loss=P, lse=None, ntok=4, V=10,
+             rng=None, coef=1.0, ws=P, ws_bytes=lib.vl_split_workspace_bytes(), stream=None)
+    a.update(kw)
+    return lib.vl_kl_fwd_bwd_ws(a["logits"], a["dtype"], a["ids"], a["probs"], a["k"],
+                                a["loss"], a["lse"], a["ntok"], a["V"], a["rng"], a["coef"],
+                                a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_split_workspace_calls_host_checks(lib):
+    n = lib.vl_split_workspace_bytes()
+    assert n == 256 * 1024
+    for f in (ce_ws, kl_ws):
+        assert f(lib, dtype=2) == VL_EDTYPE
+        assert f(lib, V=0) == VL_EINVAL
+        assert f(lib, ntok=-1) == VL_EINVAL
+        assert f(lib, rng=rng(0, 0, 0)) == VL_EINVAL
+        assert f(lib, rng=rng(8, 5, 3)) == VL_EINVAL
+        assert f(lib, ws=None) == VL_EINVAL
+        assert f(lib, ws_bytes=n - 1) == VL_EINVAL
+        assert f(lib, logits=None) == VL_EINVAL
+        assert f(lib, loss=None) == VL_EINVAL
+        assert f(lib, ntok=0, ws=None) == VL_OK  # no rows: nothing to check or run
+    assert kl_ws(lib, k=0) == VL_EINVAL
+    assert kl_ws(lib, k=11) == VL_EINVAL
+    assert kl_ws(lib, V=(1 << 19) + 8, k=4) == VL_EINVAL
+    assert kl_ws(lib, ids=None) == VL_EINVAL
+    assert kl_ws(lib, probs=None) == VL_EINVAL
+    assert ce_ws(lib, labels=None) == VL_EINVAL
+

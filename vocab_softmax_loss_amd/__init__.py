@@ -25,6 +25,7 @@ __all__ = [
     "vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
     "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
     "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror",
+    "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -69,11 +70,18 @@ def _load():
     lib.vl_kl_slice_fwd.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp, i64, rp, vp]
     lib.vl_kl_slice_merge.argtypes = [vp, i64, vp, vp, i64, rp, vp]
     lib.vl_kl_slice_bwd.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp, i64, rp, f32, vp]
+    sz = ctypes.c_size_t
+    lib.vl_split_workspace_bytes.argtypes = []
+    lib.vl_split_workspace_bytes.restype = sz
+    lib.vl_ce_fwd_bwd_ws.argtypes = [vp, i32, vp, vp, vp, i64, i64, rp, f32, vp, sz, vp]
+    lib.vl_kl_fwd_bwd_ws.argtypes = [vp, i32, vp, vp, i64, vp, vp, i64, i64, rp, f32, vp, sz,
+                                     vp]
     lib.vl_strerror.argtypes = [i32]
     lib.vl_strerror.restype = ctypes.c_char_p
     for f in (lib.vl_ce_fwd_bwd, lib.vl_ce_fwd, lib.vl_ce_bwd, lib.vl_loss_mean,
               lib.vl_kl_fwd_bwd, lib.vl_topk_renorm, lib.vl_slice_acc, lib.vl_kl_slice_fwd,
-              lib.vl_kl_slice_merge, lib.vl_kl_slice_bwd):
+              lib.vl_kl_slice_merge, lib.vl_kl_slice_bwd, lib.vl_ce_fwd_bwd_ws,
+              lib.vl_kl_fwd_bwd_ws):
         f.restype = i32
     return lib
 
@@ -189,6 +197,50 @@ def vl_kl_fwd_bwd(logits, ids, probs, loss, lse=None, rng=None, coef=1.0, stream
             _dev(loss, "loss", (torch.float32,), (ntok,)),
             None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
             ntok, V, _range(rng), float(coef), _stream(logits, stream)), "vl_kl_fwd_bwd")
+
+
+def vl_split_workspace_bytes():
+    """Bytes of workspace the *_ws calls need at least."""
+    return int(_lib.vl_split_workspace_bytes())
+
+
+def _ws(workspace):
+    return _dev(workspace, "workspace", (torch.uint8,)), workspace.numel()
+
+
+def vl_ce_fwd_bwd_ws(logits, labels, loss, workspace, lse=None, rng=None, scale=1.0,
+                     stream=None):
+    """vl_ce_fwd_bwd with a workspace (a uint8 device tensor of at least
+    vl_split_workspace_bytes() bytes) for rows split over several
+    workgroups; see vl_ce_fwd_bwd_ws in vl.h."""
+    ntok, V = logits.shape
+    wp, wn = _ws(workspace)
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_ce_fwd_bwd_ws(
+            _dev(logits, "logits", None), _dtype_code(logits),
+            _dev(labels, "labels", _INT_IDS, (ntok,)),
+            _dev(loss, "loss", (torch.float32,), (ntok,)),
+            None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, V, _range(rng), float(scale), wp, wn, _stream(logits, stream)),
+            "vl_ce_fwd_bwd_ws")
+
+
+def vl_kl_fwd_bwd_ws(logits, ids, probs, loss, workspace, lse=None, rng=None, coef=1.0,
+                     stream=None):
+    """vl_kl_fwd_bwd with a workspace for rows split over several
+    workgroups; see vl_kl_fwd_bwd_ws in vl.h."""
+    ntok, V = logits.shape
+    k = ids.shape[1] if ids.dim() == 2 else 0
+    wp, wn = _ws(workspace)
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_kl_fwd_bwd_ws(
+            _dev(logits, "logits", None), _dtype_code(logits),
+            _dev(ids, "ids", _INT_IDS, (ntok, k)),
+            _dev(probs, "probs", (torch.float32,), (ntok, k)), k,
+            _dev(loss, "loss", (torch.float32,), (ntok,)),
+            None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, V, _range(rng), float(coef), wp, wn, _stream(logits, stream)),
+            "vl_kl_fwd_bwd_ws")
 
 
 def vl_topk_renorm(logits, k, ids, probs, stream=None):

@@ -96,6 +96,21 @@ int check_rows(int dtype, int64_t ntok, int64_t V, const vl_range *rng, vl::RowA
 
 int status_of(hipError_t e) { return e == hipSuccess ? VL_OK : VL_ELAUNCH; }
 
+// check_rows plus the KL's limits: V <= kMaxKlVocab, 1 <= k <= V.
+int check_kl(int dtype, int64_t ntok, int64_t V, int64_t k, const vl_range *rng,
+             vl::RowArgs &a)
+{
+    int st = check_rows(dtype, ntok, V, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (V > vl::kMaxKlVocab || k < 1 || k > V)
+        return VL_EINVAL;
+    if (ntok > INT64_MAX / k)
+        return VL_EINVAL;
+    a.k = k;
+    return VL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,6 +134,85 @@ int vl_ce_fwd_bwd(void *logits, int dtype, const uint32_t *labels, float *loss, 
     a.k = 1;
     a.coef = scale;
     return status_of(vl::launch_rows(dtype, false, a, stream));
+}
+
+size_t vl_split_workspace_bytes(void) { return vl::kSplitWorkspaceBytes; }
+
+}  // extern "C"
+
+namespace {
+
+// Rows the single-CU kernels cannot hold on chip go to the split kernels:
+// float32 rows past 8192 16-byte vectors (32768 values), bf16 rows past the
+// 19456 vectors (155648 values) a 1024-thread block holds in registers.  The
+// bf16 rows in between run as fast whole in one block's registers (16384 x
+// 151936: 2.06 ms either way) and need no exchange.
+bool use_split(int dtype, const vl::RowArgs &a, int &S)
+{
+    const int N = dtype == VL_F32 ? 4 : 8;
+    if ((uintptr_t)a.logits % 16 != 0 || a.V % N != 0)
+        return false;
+    const int64_t nvec = a.V / N;
+    if (nvec <= (dtype == VL_F32 ? 8192 : 19456))
+        return false;
+    S = vl::split_parts(dtype, a.V);
+    return S > 0;
+}
+
+int rows_ws(int dtype, bool kl, const vl::RowArgs &a, void *ws, size_t ws_bytes,
+            hipStream_t stream)
+{
+    int S = 0;
+    if (use_split(dtype, a, S))
+        return status_of(vl::launch_rows_split(dtype, kl, a, S, ws, ws_bytes, stream));
+    return status_of(vl::launch_rows(dtype, kl, a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int vl_ce_fwd_bwd_ws(void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
+                     int64_t ntok, int64_t V, const vl_range *rng, float scale, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream)
+{
+    vl::RowArgs a{};
+    int st = check_rows(dtype, ntok, V, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (ntok == 0)
+        return VL_OK;
+    if (!logits || !labels || !loss || !workspace || workspace_bytes < vl::kSplitWorkspaceBytes)
+        return VL_EINVAL;
+    a.logits = logits;
+    a.labels = labels;
+    a.loss = loss;
+    a.lse = lse;
+    a.k = 1;
+    a.coef = scale;
+    return rows_ws(dtype, false, a, workspace, workspace_bytes, stream);
+}
+
+int vl_kl_fwd_bwd_ws(void *logits, int dtype, const uint32_t *ids, const float *probs, int64_t k,
+                     float *loss, float *lse, int64_t ntok, int64_t V, const vl_range *rng,
+                     float coef, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    vl::RowArgs a{};
+    int st = check_kl(dtype, ntok, V, k, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (ntok == 0)
+        return VL_OK;
+    if (!logits || !ids || !probs || !loss || !workspace ||
+        workspace_bytes < vl::kSplitWorkspaceBytes)
+        return VL_EINVAL;
+    a.logits = logits;
+    a.ids = ids;
+    a.probs = probs;
+    a.loss = loss;
+    a.lse = lse;
+    a.coef = coef;
+    return rows_ws(dtype, true, a, workspace, workspace_bytes, stream);
 }
 
 int vl_ce_fwd(const void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
@@ -207,13 +301,9 @@ int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *pro
                   float coef, hipStream_t stream)
 {
     vl::RowArgs a{};
-    int st = check_rows(dtype, ntok, V, rng, a);
+    int st = check_kl(dtype, ntok, V, k, rng, a);
     if (st != VL_OK)
         return st;
-    if (V > vl::kMaxKlVocab || k < 1 || k > V)
-        return VL_EINVAL;
-    if (ntok > INT64_MAX / k)
-        return VL_EINVAL;
     if (ntok == 0)
         return VL_OK;
     if (!logits || !ids || !probs || !loss)
@@ -223,7 +313,6 @@ int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *pro
     a.probs = probs;
     a.loss = loss;
     a.lse = lse;
-    a.k = k;
     a.coef = coef;
     return status_of(vl::launch_rows(dtype, true, a, stream));
 }

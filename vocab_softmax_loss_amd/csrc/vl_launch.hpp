@@ -92,6 +92,101 @@ struct RowArgs {
     void *gout;               // out != 0: [ntok][V] half-precision gradient rows
 };
 
+// One call of the split-row kernels: rows held by S co-resident
+// workgroups that swap per-part statistics through a mailbox.
+struct SplitArgs {
+    RowArgs r;
+    uint64_t *mbox;       // groups x S x S x 2 parities x 2 words, cleared before the launch
+    int64_t groups;       // row groups of S workgroups each, a multiple of 8
+    uint32_t part_vecs;   // 16-byte vectors per part (the last part may be shorter)
+    uint32_t spin_limit;  // polls of one exchange before its row is given up (NaN)
+    int parts;            // S, workgroups per row
+};
+
+// Split kernels.  A part of a row sits in BLOCK threads x NV 16-byte
+// vectors of registers; with PF the next row's part streams into LDS
+// meanwhile; PER_CU workgroups share a CU.  float32: 1024 x 8 vectors (a
+// 128 KB part, the size of a 32000-value row) with the LDS prefetch, one
+// workgroup per CU; bf16: 512 x 7 vectors (56 KB) with the LDS prefetch, two
+// per CU (8 vectors spill registers in the KL kernel).
+struct SplitShape {
+    int block, nv;
+    bool pf;
+    int per_cu;
+};
+constexpr SplitShape kSplitF32{1024, 8, true, 1};
+constexpr SplitShape kSplitBf16{512, 7, true, 2};
+// Most parts a row is split into.
+constexpr int kMaxSplit = 16;
+
+// Parts a row of V values (N per 16-byte vector) is split into: the fewest
+// whose parts fit one workgroup of `shape`, at least 2; 0 when V is not a
+// whole number of vectors or more than kMaxSplit parts would be needed.
+inline int split_parts_n(int64_t V, int N, const SplitShape &shape)
+{
+    const int64_t part = (int64_t)shape.block * shape.nv;
+    if (V < 1 || V % N != 0)
+        return 0;
+    const int64_t nvec = V / N;
+    int64_t S = (nvec + part - 1) / part;
+    if (S < 2)
+        S = 2;
+    return S <= kMaxSplit ? (int)S : 0;
+}
+
+// Workgroup b of a split launch is member `me` of row group `grp`: the
+// hardware deals consecutive workgroups to the 8 XCDs in turn, so b, b + 8,
+// b + 16, ... share an XCD, and the S members of a group are S of those.
+__host__ __device__ inline void split_member(int64_t b, int S, int &me, int64_t &grp)
+{
+    const int64_t q = b >> 3;
+    me = (int)(q % S);
+    grp = (b & 7) + 8 * (q / S);
+}
+
+// First of the two 64-bit words of mailbox slot (group g, writer w, reader
+// r, row parity par).
+__host__ __device__ inline int64_t mbox_index(int64_t g, int S, int w, int r, int par)
+{
+    return ((((g * S) + w) * S + r) * 2 + par) * 2;
+}
+
+// The shape of one split launch: N values per 16-byte vector, S parts, the
+// kernel shape (with the workgroups per CU that fit) and the CUs.
+struct SplitPlan {
+    uint32_t part_vecs;   // 16-byte vectors per part (the last part may be shorter)
+    int64_t groups;       // a multiple of 8; 0 when the workspace holds too few
+    size_t words;         // KL: 32-bit words of one part bitmap
+    size_t lds;           // dynamic LDS bytes (PF slots, KL bitmaps)
+    int64_t mbox_words;   // 64-bit mailbox words the launch uses
+};
+
+inline SplitPlan split_plan(int64_t V, int N, int S, bool kl, const SplitShape &shape, int cus,
+                            size_t ws_bytes)
+{
+    SplitPlan p{};
+    const int64_t nvec = V / N;
+    p.part_vecs = (uint32_t)((nvec + S - 1) / S);
+    p.words = ((size_t)p.part_vecs * (size_t)N + 31) >> 5;
+    p.lds = (shape.pf ? (size_t)shape.block * shape.nv * 16 : 0) +
+            (kl ? 2 * p.words * sizeof(uint32_t) : 0);
+    int64_t groups = (int64_t)shape.per_cu * cus / S / 8 * 8;
+    const int64_t ws_groups = (int64_t)(ws_bytes / ((size_t)S * S * 4 * sizeof(uint64_t))) / 8 * 8;
+    if (groups > ws_groups)
+        groups = ws_groups;
+    p.groups = groups < 8 ? 0 : groups;
+    p.mbox_words = p.groups * S * S * 4;
+    return p;
+}
+
+// Polls of one mailbox exchange before the row is given up: far beyond any
+// wait among co-resident workgroups (each poll is two atomic round trips
+// plus a short sleep, one to two microseconds, so about half a second).
+constexpr uint32_t kSplitSpinLimit = 1u << 18;
+
+// Workspace bytes the split-row calls use at most.
+constexpr size_t kSplitWorkspaceBytes = 256 * 1024;
+
 // One call of the per-slice KL passes (checked by the caller).
 struct SliceArgs {
     void *logits;           // row r of the slice starts at element r * ld
@@ -135,6 +230,14 @@ int head_kl(const HeadArgs &a, hipStream_t stream);
 // rows write it rounded to bf16 / f16 into a.gout and leave the logits.
 hipError_t launch_rows(int dtype, bool kl, const RowArgs &a, hipStream_t stream, int out = 0);
 hipError_t launch_topk(int dtype, const TopkArgs &a, hipStream_t stream);
+// Parts a row of V values is split into (2 to kMaxSplit), or 0 when the
+// split kernels do not take it (V not a whole number of 16-byte vectors, or
+// a row longer than kMaxSplit parts hold).
+int split_parts(int dtype, int64_t V);
+// The fused rows split into S parts (S from split_parts), the mailbox in
+// `ws` (ws_bytes bytes, cleared first on `stream`); a.logits 16-byte aligned.
+hipError_t launch_rows_split(int dtype, bool kl, const RowArgs &a, int S, void *ws,
+                             size_t ws_bytes, hipStream_t stream);
 hipError_t launch_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream);
 // Cross-entropy in two calls, with RowArgs as for launch_rows: the forward
 // reads the logits and writes loss and lse (lse may be null); the backward
