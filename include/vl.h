@@ -197,6 +197,26 @@ int vl_kl_fwd_bwd_ws(void *logits, int dtype, const uint32_t *ids, const float *
                      float coef, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * vl_kl_fwd_bwd_ws without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the mailbox of the split rows is the library's
+ * own device array of vl_split_workspace_bytes() (256 KiB), resident on each
+ * device the library runs on until the process ends.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine); the first call on
+ * a device looks the array's address up once.  The array's size does not
+ * depend on ntok, V or k (it holds the mailbox of any launch), so no input
+ * size is rejected for it.  Every call on a device shares that device's
+ * array and clears what it uses on `stream` before it starts: calls that
+ * overlap on one device (on different streams, or from several threads)
+ * race and give undefined results; calls in order on one stream are fine.
+ * Arguments, results and limits: as vl_kl_fwd_bwd_ws (bit for bit the same
+ * results).
+ */
+int vl_kl_fwd_bwd_noalloc(void *logits, int dtype, const uint32_t *ids, const float *probs,
+                          int64_t k, float *loss, float *lse, int64_t ntok, int64_t V,
+                          const vl_range *rng, float coef, hipStream_t stream);
+
+/*
  * Teacher top-k with renormalised probabilities [KL: topk_rows].
  *   logits  [ntok][V] dtype, read only.
  *   ids     [ntok][k] uint32, written: the k ids first in the order (value

@@ -15,5 +15,10 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # Run the GPU tests in file order, but the full-size ones after the
-    # small ones, so a failure on a small case shows first.
-    items.sort(key=lambda it: 1 if it.get_closest_marker("slow") else 0)
+    # small ones, so a failure on a small case shows first, and the
+    # no-allocation entry point's test (test_zz_*) last of all.
+    def rank(it):
+        if os.path.basename(str(it.fspath)).startswith("test_zz_"):
+            return 2
+        return 1 if it.get_closest_marker("slow") else 0
+    items.sort(key=rank)

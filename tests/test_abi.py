@@ -30,7 +30,8 @@ def test_header_declares_the_calls():
         ["vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
          "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
          "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror",
-         "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws"])
+         "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws",
+         "vl_kl_fwd_bwd_noalloc"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -282,4 +283,24 @@ def test_split_workspace_calls_host_checks(lib):
     assert kl_ws(lib, ids=None) == VL_EINVAL
     assert kl_ws(lib, probs=None) == VL_EINVAL
     assert ce_ws(lib, labels=None) == VL_EINVAL
+
+
+def test_noalloc_host_checks(lib):
+    def f(**kw):
+        a = dict(logits=P, dtype=0, ids=P, probs=P, k=2, loss=P, lse=None, ntok=4, V=10,
+                 rng=None, coef=1.0, stream=None)
+        a.update(kw)
+        return lib.vl_kl_fwd_bwd_noalloc(a["logits"], a["dtype"], a["ids"], a["probs"], a["k"],
+                                         a["loss"], a["lse"], a["ntok"], a["V"], a["rng"],
+                                         a["coef"], a["stream"])
+    assert f(dtype=2) == VL_EDTYPE
+    assert f(V=0) == VL_EINVAL
+    assert f(k=0) == VL_EINVAL
+    assert f(k=11) == VL_EINVAL
+    assert f(V=(1 << 19) + 8, k=4) == VL_EINVAL
+    assert f(ntok=-1) == VL_EINVAL
+    assert f(rng=rng(8, 5, 3)) == VL_EINVAL
+    for name in ("logits", "ids", "probs", "loss"):
+        assert f(**{name: None}) == VL_EINVAL
+    assert f(ntok=0, logits=None) == VL_OK
 

@@ -25,7 +25,7 @@ __all__ = [
     "vl_ce_fwd_bwd", "vl_ce_fwd", "vl_ce_bwd", "vl_loss_mean", "vl_kl_fwd_bwd",
     "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
     "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror",
-    "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws",
+    "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws", "vl_kl_fwd_bwd_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -76,12 +76,13 @@ def _load():
     lib.vl_ce_fwd_bwd_ws.argtypes = [vp, i32, vp, vp, vp, i64, i64, rp, f32, vp, sz, vp]
     lib.vl_kl_fwd_bwd_ws.argtypes = [vp, i32, vp, vp, i64, vp, vp, i64, i64, rp, f32, vp, sz,
                                      vp]
+    lib.vl_kl_fwd_bwd_noalloc.argtypes = [vp, i32, vp, vp, i64, vp, vp, i64, i64, rp, f32, vp]
     lib.vl_strerror.argtypes = [i32]
     lib.vl_strerror.restype = ctypes.c_char_p
     for f in (lib.vl_ce_fwd_bwd, lib.vl_ce_fwd, lib.vl_ce_bwd, lib.vl_loss_mean,
               lib.vl_kl_fwd_bwd, lib.vl_topk_renorm, lib.vl_slice_acc, lib.vl_kl_slice_fwd,
               lib.vl_kl_slice_merge, lib.vl_kl_slice_bwd, lib.vl_ce_fwd_bwd_ws,
-              lib.vl_kl_fwd_bwd_ws):
+              lib.vl_kl_fwd_bwd_ws, lib.vl_kl_fwd_bwd_noalloc):
         f.restype = i32
     return lib
 
@@ -241,6 +242,22 @@ def vl_kl_fwd_bwd_ws(logits, ids, probs, loss, workspace, lse=None, rng=None, co
             None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
             ntok, V, _range(rng), float(coef), wp, wn, _stream(logits, stream)),
             "vl_kl_fwd_bwd_ws")
+
+
+def vl_kl_fwd_bwd_noalloc(logits, ids, probs, loss, lse=None, rng=None, coef=1.0, stream=None):
+    """vl_kl_fwd_bwd_ws with the library's own device mailbox in place of a
+    workspace (nothing is allocated); see vl_kl_fwd_bwd_noalloc in vl.h."""
+    ntok, V = logits.shape
+    k = ids.shape[1] if ids.dim() == 2 else 0
+    with torch.cuda.device(logits.device):
+        _check(_lib.vl_kl_fwd_bwd_noalloc(
+            _dev(logits, "logits", None), _dtype_code(logits),
+            _dev(ids, "ids", _INT_IDS, (ntok, k)),
+            _dev(probs, "probs", (torch.float32,), (ntok, k)), k,
+            _dev(loss, "loss", (torch.float32,), (ntok,)),
+            None if lse is None else _dev(lse, "lse", (torch.float32,), (ntok,)),
+            ntok, V, _range(rng), float(coef), _stream(logits, stream)),
+            "vl_kl_fwd_bwd_noalloc")
 
 
 def vl_topk_renorm(logits, k, ids, probs, stream=None):

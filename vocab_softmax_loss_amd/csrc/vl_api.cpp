@@ -215,6 +215,34 @@ int vl_kl_fwd_bwd_ws(void *logits, int dtype, const uint32_t *ids, const float *
     return rows_ws(dtype, true, a, workspace, workspace_bytes, stream);
 }
 
+int vl_kl_fwd_bwd_noalloc(void *logits, int dtype, const uint32_t *ids, const float *probs,
+                          int64_t k, float *loss, float *lse, int64_t ntok, int64_t V,
+                          const vl_range *rng, float coef, hipStream_t stream)
+{
+    vl::RowArgs a{};
+    int st = check_kl(dtype, ntok, V, k, rng, a);
+    if (st != VL_OK)
+        return st;
+    if (ntok == 0)
+        return VL_OK;
+    if (!logits || !ids || !probs || !loss)
+        return VL_EINVAL;
+    a.logits = logits;
+    a.ids = ids;
+    a.probs = probs;
+    a.loss = loss;
+    a.lse = lse;
+    a.coef = coef;
+    int S = 0;
+    if (!use_split(dtype, a, S))
+        return status_of(vl::launch_rows(dtype, true, a, stream));
+    void *ws = nullptr;
+    if (vl::split_scratch(&ws) != hipSuccess)
+        return VL_ELAUNCH;
+    return status_of(vl::launch_rows_split(dtype, true, a, S, ws, vl::kSplitWorkspaceBytes,
+                                           stream));
+}
+
 int vl_ce_fwd(const void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
               int64_t ntok, int64_t V, const vl_range *rng, hipStream_t stream)
 {

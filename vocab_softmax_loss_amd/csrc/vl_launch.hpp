@@ -238,6 +238,9 @@ int split_parts(int dtype, int64_t V);
 // `ws` (ws_bytes bytes, cleared first on `stream`); a.logits 16-byte aligned.
 hipError_t launch_rows_split(int dtype, bool kl, const RowArgs &a, int S, void *ws,
                              size_t ws_bytes, hipStream_t stream);
+// The device address of the library's own kSplitWorkspaceBytes mailbox on
+// the current device (looked up once per device).
+hipError_t split_scratch(void **ptr);
 hipError_t launch_slice_acc(float *dst, const float *src, int64_t n, hipStream_t stream);
 // Cross-entropy in two calls, with RowArgs as for launch_rows: the forward
 // reads the logits and writes loss and lse (lse may be null); the backward

@@ -54,6 +54,8 @@
 // else only that element while the owner writes the vector's others.
 #include <math.h>
 
+#include <mutex>
+
 #include "vl_device.hpp"
 #include "vl_launch.hpp"
 
@@ -707,6 +709,35 @@ hipError_t launch_split_dt(const RowArgs &a, int S, void *ws, size_t ws_bytes, h
 }
 
 }  // namespace
+
+// The mailbox of the entry point for callers that cannot allocate
+// (vl_kl_fwd_bwd_noalloc): one workspace's worth, resident on every device
+// the library runs on until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): split_scratch looks up its device address once per device.
+static __device__ __align__(256) uint64_t scratch[kSplitWorkspaceBytes / sizeof(uint64_t)];
+
+hipError_t split_scratch(void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int split_parts(int dtype, int64_t V)
 {
