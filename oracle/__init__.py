@@ -244,6 +244,37 @@ def head_kl(x, w, ids, probs, total, gscale):
 
 # ---------------------------------------------------- vocabulary slices
 
+def head_topk(x, w, k):
+    """The teacher side of the vocabulary head (cortiq-engine train_head.rs,
+    host fn topk), float64, on hidden rows ``x`` [n][hs] and head ``w``
+    [V][hs] given as float64 values (already rounded the way the GPU rounds
+    them, see ``round_half``):
+
+      s_t = w x_t                         (logits, a library matmul)
+      ids_t = the k ids first in the order (s_t desc, id asc)
+      probs_t[q] = exp(s_t[ids_q] - s_t[ids_0]) / sum_{q' < k} exp(...)
+
+    The order is a stable library sort on (-s, id) of every column, ties to
+    the lower id (-0 and +0 tie).  Returns (ids uint32 [n][k], probs float64
+    [n][k]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    s = x @ w.T
+    n, V = s.shape
+    k = int(k)
+    ids = np.empty((n, k), dtype=np.uint32)
+    probs = np.empty((n, k))
+    cols = np.arange(V)
+    for t in range(n):
+        order = np.lexsort((cols, -s[t]))[:k]
+        ids[t] = order
+        v = s[t, order]
+        e = np.exp(v - v[0])
+        probs[t] = e / e.sum()
+    return ids, probs
+
+
 def _widen(logits) -> np.ndarray:
     """[n][w] float32 or bf16 bit patterns (uint16) as exact float64."""
     a = _rows2d(logits)

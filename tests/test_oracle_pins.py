@@ -575,6 +575,61 @@ def test_head_matches_the_row_kl_on_exact_logits():
     np.testing.assert_allclose(dx, (g @ w) / gscale, rtol=1e-12, atol=1e-15)
 
 
+def _dyadic_head(seed, n, V, hs):
+    """Hidden rows and head weights of small dyadic values: every product
+    and every partial sum of a logit is exact in float32 (and in float64)."""
+    r = np.random.default_rng(seed)
+    x = r.integers(-4, 5, size=(n, hs)) / 4.0
+    w = r.integers(-8, 9, size=(V, hs)) / 8.0
+    return x, w
+
+
+def test_head_topk_matches_the_row_topk_on_exact_logits():
+    """With exact float32 logits the head's top-k equals the C oracle's
+    top-k of those logits (a separately written routine: a qsort of the
+    whole row with the tie rule); coarse dyadic values make ties common."""
+    for seed, (n, V, hs, k) in enumerate([(6, 64, 8, 10), (4, 300, 5, 64), (3, 50, 2, 50)]):
+        x, w = _dyadic_head(20 + seed, n, V, hs)
+        s = (x @ w.T).astype(np.float32)
+        assert np.array_equal(s.astype(np.float64), x @ w.T)
+        ids, probs = oracle.head_topk(x, w, k)
+        cids, cprobs = oracle.topk(s, k)
+        np.testing.assert_array_equal(ids, cids)
+        np.testing.assert_allclose(probs, cprobs, rtol=1e-13, atol=1e-300)
+
+
+def test_head_topk_brute_force_and_invariants():
+    """Against a brute force over every pair of columns (an id ranks ahead
+    of another iff its logit is larger, or equal with a lower id); probs
+    sum to 1, do not increase, and k = V gives the whole row's softmax."""
+    x, w = _dyadic_head(31, 5, 40, 3)
+    s = x @ w.T
+    V = s.shape[1]
+    for k in (1, 7, V):
+        ids, probs = oracle.head_topk(x, w, k)
+        for t in range(s.shape[0]):
+            rank = [sum(1 for j in range(V) if s[t, j] > s[t, i] or (s[t, j] == s[t, i] and j < i))
+                    for i in range(V)]
+            want = [i for i in sorted(range(V), key=lambda i: rank[i])][:k]
+            assert ids[t].tolist() == want
+            assert abs(probs[t].sum() - 1.0) < 1e-14
+            assert np.all(np.diff(probs[t]) <= 1e-18)
+        if k == V:
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            sm = e / e.sum(axis=1, keepdims=True)
+            np.testing.assert_allclose(probs, np.take_along_axis(sm, ids.astype(np.int64), 1),
+                                       rtol=1e-13)
+
+
+def test_head_topk_zero_weights_give_the_first_ids():
+    """W = 0: every logit is 0, all tie, so the ids are 0..k-1 with equal
+    probabilities 1/k."""
+    x, w = _dyadic_head(32, 3, 20, 4)
+    ids, probs = oracle.head_topk(x, np.zeros_like(w), 6)
+    assert (ids == np.arange(6)).all()
+    np.testing.assert_allclose(probs, 1.0 / 6, rtol=1e-15)
+
+
 def test_round_half_is_round_to_nearest_even():
     """f16 by numpy's cast; bf16 ties go to the even pattern."""
     one = np.float32(1.0)
