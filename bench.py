@@ -19,7 +19,7 @@ the launch stream around every launch of the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
                     [--workload step|ce_lm|ce_split|topk_zipf|kl_large|kl_large_unsplit|kl_bf16|
-                                kl_sliced|head_kl|copy_calib]
+                                kl_sliced|head_kl|head_topk|copy_calib]
     python bench.py --pmc-summary <counter_collection.csv> ...
 
 The other workloads time one configuration each at its full size, for
@@ -284,6 +284,21 @@ def other_workload(name, dev):
         nbytes = {"head": None}
         cfg = {"workload": "head_16384x151936x1024_bf16_k256", "ntok": ntok, "V": V, "hs": hs,
                "k": k, "chunk": chunk, "dtype": "bf16", "flops": 2 * 2 * ntok * V * hs}
+    elif name == "head_topk":
+        # the teacher side of the head: the logits product on the matrix
+        # cores, then the top-k rows over the float32 logits, one chunk
+        c = gi.head_inputs(16384, 151936, 1024, 4, 6002, dev, torch.bfloat16)
+        ntok, hs = c["x"].shape
+        V, k, chunk = c["w"].shape[0], 256, ntok
+        ids = torch.empty((ntok, k), dtype=torch.int32, device=dev)
+        probs = torch.empty((ntok, k), device=dev)
+        scratch = torch.empty(vl.vl_head_topk_scratch_bytes(chunk, V, hs), dtype=torch.uint8,
+                              device=dev)
+        calls = [("head_topk", lambda: vl.vl_head_topk(c["x"], c["w"], k, ids, probs, chunk,
+                                                       scratch))]
+        nbytes = {"head_topk": None}
+        cfg = {"workload": "head_topk_16384x151936x1024_bf16_k256", "ntok": ntok, "V": V,
+               "hs": hs, "k": k, "chunk": chunk, "dtype": "bf16", "flops": 2 * ntok * V * hs}
     elif name == "copy_calib":
         n = COPY_CALIB_BYTES // 4
         src = torch.randn(n, device=dev)

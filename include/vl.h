@@ -331,6 +331,38 @@ int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
                int64_t hs, int64_t total, float gscale, int64_t chunk, void *scratch,
                size_t scratch_bytes, hipStream_t stream);
 
+/*
+ * Scratch bytes vl_head_topk needs for `chunk` rows at a time: float32
+ * logits [chunk][V], the half-precision hidden rows [chunk][hs] and a
+ * 64 MiB GEMM workspace, each 256-byte aligned (0 for invalid sizes).
+ */
+size_t vl_head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
+
+/*
+ * The teacher side of the vocabulary head [KL: topk (the host function:
+ * hidden rows to half precision, the logits product per slice, topk_rows
+ * per chunk of rows), Head, HeadScratch]: for chunks of `chunk` rows,
+ *   act    = half(x rows)                  (round to nearest even)
+ *   logits = act . w^T                     (float32 accumulation)
+ *   ids, probs = vl_topk_renorm of the float32 logits rows
+ * so each row gets the k ids first in the order (logit descending, id
+ * ascending) and their probabilities renormalised over the k.
+ *   x       [ntok][hs] float32, read only: the teacher's normed hidden rows.
+ *   w       [V][hs] head weights in wdtype (VL_F16 or VL_BF16), read only.
+ *   ids     [ntok][k] uint32, written.
+ *   probs   [ntok][k] float32, written.
+ *   scratch device buffer of at least vl_head_topk_scratch_bytes(min(chunk,
+ *           ntok), V, hs) bytes, owned by the caller; contents on entry do
+ *           not matter and are undefined after the call.
+ * The product runs in hipBLASLt, as in vl_head_kl (same handle, same
+ * one-time timing of its algorithms per shape, which waits for `stream`).
+ * Limits: 1 <= k <= min(V, 2048), V <= 2^31 - 1, hs >= 1, chunk >= 1,
+ * ntok <= 2^31 - 1.
+ */
+int vl_head_topk(const float *x, const void *w, int wdtype, int64_t ntok, int64_t V, int64_t hs,
+                 int64_t k, uint32_t *ids, float *probs, int64_t chunk, void *scratch,
+                 size_t scratch_bytes, hipStream_t stream);
+
 /* Static text naming a status code. */
 const char *vl_strerror(int status);
 

@@ -31,7 +31,7 @@ def test_header_declares_the_calls():
          "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
          "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror",
          "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws",
-         "vl_kl_fwd_bwd_noalloc"])
+         "vl_kl_fwd_bwd_noalloc", "vl_head_topk_scratch_bytes", "vl_head_topk"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -303,4 +303,31 @@ def test_noalloc_host_checks(lib):
     for name in ("logits", "ids", "probs", "loss"):
         assert f(**{name: None}) == VL_EINVAL
     assert f(ntok=0, logits=None) == VL_OK
+
+
+def test_head_topk_host_checks(lib):
+    n = lib.vl_head_topk_scratch_bytes(8, 1000, 64)
+    assert n >= 8 * 1000 * 4 + 8 * 64 * 2 + (64 << 20)
+    assert lib.vl_head_topk_scratch_bytes(0, 1000, 64) == 0
+    assert lib.vl_head_topk_scratch_bytes(8, 0, 64) == 0
+
+    def f(**kw):
+        a = dict(x=P, w=P, wd=1, ntok=4, V=1000, hs=64, k=16, ids=P, probs=P, chunk=8,
+                 scratch=P, sb=n, stream=None)
+        a.update(kw)
+        return lib.vl_head_topk(a["x"], a["w"], a["wd"], a["ntok"], a["V"], a["hs"], a["k"],
+                                a["ids"], a["probs"], a["chunk"], a["scratch"], a["sb"],
+                                a["stream"])
+    assert f(wd=0) == VL_EDTYPE
+    assert f(k=0) == VL_EINVAL
+    assert f(k=1001) == VL_EINVAL
+    assert f(V=5000, k=2049) == VL_EINVAL
+    assert f(hs=0) == VL_EINVAL
+    assert f(chunk=0) == VL_EINVAL
+    assert f(ntok=-1) == VL_EINVAL
+    n4 = lib.vl_head_topk_scratch_bytes(4, 1000, 64)  # min(chunk, ntok) rows
+    assert f(sb=n4 - 1) == VL_EINVAL
+    for name in ("x", "w", "ids", "probs", "scratch"):
+        assert f(**{name: None}) == VL_EINVAL
+    assert f(ntok=0, x=None) == VL_OK
 

@@ -111,3 +111,115 @@ def test_head_zero_rows_and_repeat(vl):
     b = run_head(vl, c["x"], c["w"], c["ids"], c["probs"], 20, 64.0, 8)
     np.testing.assert_allclose(a[0], b[0], rtol=1e-6, atol=0)
     np.testing.assert_allclose(a[1], b[1], rtol=1e-6, atol=1e-12)
+
+
+# ------------------------------------------------ the teacher side (vl_head_topk)
+
+def run_head_topk(vl, x, w, k, chunk):
+    ntok, hs = x.shape
+    V = w.shape[0]
+    ids = torch.full((ntok, k), -1, dtype=torch.int32, device=DEV)
+    probs = torch.full((ntok, k), float("nan"), device=DEV)
+    nb = vl.vl_head_topk_scratch_bytes(min(chunk, ntok), V, hs)
+    scratch = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    vl.vl_head_topk(x, w, k, ids, probs, chunk, scratch)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy().view(np.uint32), probs.cpu().numpy().astype(np.float64)
+
+
+def dyadic_head(ntok, V, hs, seed, dtype):
+    """Hidden rows in quarters and head weights in eighths (both exact in
+    f16 and bf16): every product and partial sum of a logit is exact in
+    float32 for hs <= 64, so the GPU's float32 logits are the exact ones
+    whatever the order of accumulation, and ties are common."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    x = torch.randint(-4, 5, (ntok, hs), generator=g, device=DEV).float() / 4
+    w = (torch.randint(-8, 9, (V, hs), generator=g, device=DEV).float() / 8).to(HALF[dtype])
+    return x, w
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("ntok,V,hs,k,chunk", [
+    (37, 1000, 64, 64, 16),       # ragged last chunk
+    (20, 32000, 32, 256, 20),     # one chunk
+    (5, 151936, 48, 2048, 3),     # the largest vocabulary, the largest k
+    (9, 7, 4, 7, 4),              # k = V
+])
+def test_head_topk_exact_logits(vl, dtype, ntok, V, hs, k, chunk):
+    """Exact float32 logits: ids bit-exact against the oracle's head top-k
+    (ties to the lower id), probabilities within 1e-5 relative."""
+    x, w = dyadic_head(ntok, V, hs, 8000 + V, dtype)
+    ids, probs = run_head_topk(vl, x, w, k, chunk)
+    oi, op = oracle.head_topk(x.cpu().numpy().astype(np.float64),
+                              w.float().cpu().numpy().astype(np.float64), k)
+    np.testing.assert_array_equal(ids, oi)
+    assert np.all(np.abs(probs - op) <= 1e-5 * np.abs(op) + 1e-12)
+
+
+def check_near(ids, probs, s, eps, k, what):
+    """ids/probs from float32 logits against the float64 logits s, where
+    each float32 logit is within eps[t] of s: every id whose logit clears the
+    oracle's k-th by more than 2 eps is chosen, every chosen id comes within
+    2 eps of it, the chosen logits do not increase by more than 2 eps, and
+    the probabilities are the renormalised softmax of the chosen logits."""
+    n = s.shape[0]
+    cols = np.arange(s.shape[1])
+    for t in range(n):
+        order = np.lexsort((cols, -s[t]))
+        kth = s[t, order[k - 1]]
+        got = ids[t].astype(np.int64)
+        assert len(set(got.tolist())) == k, (what, t, "repeated id")
+        must = order[s[t, order] > kth + 2 * eps[t]]
+        assert set(must.tolist()) <= set(got.tolist()), (what, t, "a clear winner is missing")
+        v = s[t, got]
+        assert np.all(v >= kth - 2 * eps[t]), (what, t, "a chosen id is not near the top k")
+        assert np.all(np.diff(v) <= 2 * eps[t]), (what, t, "not in descending order")
+        e = np.exp(v - v[0])
+        want = e / e.sum()
+        assert np.all(np.abs(probs[t] - want) <= 1e-4 * want + 1e-12), (what, t)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_head_topk_random(vl, dtype):
+    """N(0, 1) hidden rows and N(0, 1/hs) weights: the float32 logits carry
+    accumulation error, bounded by hs 2^-24 sum_i |x_i w_i| per logit."""
+    ntok, V, hs, k = 50, 32000, 512, 64
+    c = gi.head_inputs(ntok, V, hs, 4, 8100, DEV, HALF[dtype])
+    x, w = c["x"], c["w"]
+    ids, probs = run_head_topk(vl, x, w, k, 32)
+    xr = oracle.round_half(x.cpu().numpy(), dtype)
+    wr = w.float().cpu().numpy().astype(np.float64)
+    s = xr @ wr.T
+    eps = hs * 2.0 ** -24 * (np.abs(xr) @ np.abs(wr).T).max(axis=1)
+    check_near(ids, probs, s, eps, k, dtype)
+
+
+@pytest.mark.slow
+def test_head_topk_full(vl):
+    """The teacher side at 16384 x 151936 x 1024 bf16, k = 256, in one
+    chunk: sampled rows (chunk edges included) as in the random case, and
+    invariants on every row."""
+    ntok, V, hs, k = 16384, 151936, 1024, 256
+    c = gi.head_inputs(ntok, V, hs, 4, 8200, DEV, torch.bfloat16)
+    x, w = c["x"], c["w"]
+    ids = torch.empty((ntok, k), dtype=torch.int32, device=DEV)
+    probs = torch.empty((ntok, k), device=DEV)
+    scratch = torch.empty(vl.vl_head_topk_scratch_bytes(ntok, V, hs), dtype=torch.uint8,
+                          device=DEV)
+    vl.vl_head_topk(x, w, k, ids, probs, ntok, scratch)
+    torch.cuda.synchronize()
+    il = ids.long()
+    assert int(il.min()) >= 0 and int(il.max()) < V
+    srt = il.sort(dim=1).values
+    assert bool((srt[:, 1:] != srt[:, :-1]).all())
+    assert float((probs.double().sum(dim=1) - 1).abs().max()) < 1e-5
+    rows = np.unique(np.concatenate([np.random.default_rng(62).choice(ntok, 12, replace=False),
+                                     [0, ntok - 1]]))
+    rt = torch.from_numpy(rows).to(DEV)
+    xr = oracle.round_half(x[rt].cpu().numpy(), "bf16")
+    wr = w.float().cpu().numpy().astype(np.float64)
+    s = xr @ wr.T
+    eps = hs * 2.0 ** -24 * (np.abs(xr) @ np.abs(wr).T).max(axis=1)
+    check_near(ids[rt].cpu().numpy().view(np.uint32), probs[rt].cpu().numpy().astype(np.float64),
+               s, eps, k, "full")

@@ -26,6 +26,7 @@ __all__ = [
     "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
     "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror",
     "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws", "vl_kl_fwd_bwd_noalloc",
+    "vl_head_topk_scratch_bytes", "vl_head_topk",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +78,10 @@ def _load():
     lib.vl_kl_fwd_bwd_ws.argtypes = [vp, i32, vp, vp, i64, vp, vp, i64, i64, rp, f32, vp, sz,
                                      vp]
     lib.vl_kl_fwd_bwd_noalloc.argtypes = [vp, i32, vp, vp, i64, vp, vp, i64, i64, rp, f32, vp]
+    lib.vl_head_topk_scratch_bytes.argtypes = [i64, i64, i64]
+    lib.vl_head_topk_scratch_bytes.restype = sz
+    lib.vl_head_topk.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, vp, sz, vp]
+    lib.vl_head_topk.restype = i32
     lib.vl_strerror.argtypes = [i32]
     lib.vl_strerror.restype = ctypes.c_char_p
     for f in (lib.vl_ce_fwd_bwd, lib.vl_ce_fwd, lib.vl_ce_bwd, lib.vl_loss_mean,
@@ -307,6 +312,31 @@ def vl_head_kl(x, w, ids, probs, dx, loss, total, gscale, chunk, scratch, stream
             ntok, V, hs, int(total), float(gscale), int(chunk),
             _dev(scratch, "scratch", (torch.uint8,)), scratch.numel(),
             _stream(x, stream)), "vl_head_kl")
+
+
+def vl_head_topk_scratch_bytes(chunk, V, hs):
+    """Bytes of scratch vl_head_topk needs for `chunk` rows at a time."""
+    return int(_lib.vl_head_topk_scratch_bytes(int(chunk), int(V), int(hs)))
+
+
+def vl_head_topk(x, w, k, ids, probs, chunk, scratch, stream=None):
+    """Teacher-side vocabulary head: top-k ids and renormalised
+    probabilities of half(x) . w^T; see vl_head_topk in vl.h.  ``w`` is a
+    torch.float16 or torch.bfloat16 [V][hs] tensor; ``scratch`` a uint8
+    device tensor of at least vl_head_topk_scratch_bytes(min(chunk, ntok),
+    V, hs) bytes."""
+    ntok, hs = x.shape
+    V = w.shape[0]
+    wd = {torch.float16: VL_F16, torch.bfloat16: VL_BF16}.get(w.dtype)
+    if wd is None:
+        raise TypeError(f"w must be float16 or bfloat16, got {w.dtype}")
+    with torch.cuda.device(x.device):
+        _check(_lib.vl_head_topk(
+            _dev(x, "x", (torch.float32,)), _dev(w, "w", None, (V, hs)), wd, ntok, V, hs,
+            int(k), _dev(ids, "ids", _INT_IDS, (ntok, k)),
+            _dev(probs, "probs", (torch.float32,), (ntok, k)), int(chunk),
+            _dev(scratch, "scratch", (torch.uint8,)), scratch.numel(),
+            _stream(x, stream)), "vl_head_topk")
 
 
 def _slice_rows(t: torch.Tensor, name: str):

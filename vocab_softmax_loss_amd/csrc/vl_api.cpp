@@ -324,6 +324,37 @@ int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
     return vl::head_kl(a, stream);
 }
 
+size_t vl_head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
+{
+    if (chunk < 1 || V < 1 || hs < 1 || V > kMaxV || hs > kMaxV)
+        return 0;
+    if (chunk > INT64_MAX / V / 8)
+        return 0;
+    return vl::head_topk_scratch_bytes(chunk, V, hs);
+}
+
+int vl_head_topk(const float *x, const void *w, int wdtype, int64_t ntok, int64_t V, int64_t hs,
+                 int64_t k, uint32_t *ids, float *probs, int64_t chunk, void *scratch,
+                 size_t scratch_bytes, hipStream_t stream)
+{
+    if (wdtype != VL_BF16 && wdtype != VL_F16)
+        return VL_EDTYPE;
+    if (ntok < 0 || V < 1 || V > kMaxV || hs < 1 || hs > kMaxV || k < 1 || k > V ||
+        k > vl::kMaxTopk || chunk < 1 || ntok > INT32_MAX)
+        return VL_EINVAL;
+    if (ntok > INT64_MAX / (V > hs ? V : hs) || chunk > INT64_MAX / V / 8)
+        return VL_EINVAL;
+    if (ntok == 0)
+        return VL_OK;
+    if (!x || !w || !ids || !probs || !scratch)
+        return VL_EINVAL;
+    const int64_t c = chunk < ntok ? chunk : ntok;
+    if (scratch_bytes < vl::head_topk_scratch_bytes(c, V, hs))
+        return VL_EINVAL;
+    vl::HeadTopkArgs a{x, w, wdtype, ntok, V, hs, k, c, ids, probs, scratch};
+    return vl::head_topk(a, stream);
+}
+
 int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *probs, int64_t k,
                   float *loss, float *lse, int64_t ntok, int64_t V, const vl_range *rng,
                   float coef, hipStream_t stream)

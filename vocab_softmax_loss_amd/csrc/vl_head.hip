@@ -1,10 +1,13 @@
-// Vocabulary head with the distillation KL for gfx950 (cortiq-engine
-// train_head.rs: Head, HeadScratch, head_kl).  For each chunk of rows:
+// Vocabulary head for gfx950 (cortiq-engine train_head.rs: Head,
+// HeadScratch, head_kl, topk).  The student side with the distillation KL,
+// for each chunk of rows:
 //   act    = half(x[r0:r1])                         [rows][hs]   (to_half_kernel)
 //   logits = act . W^T, float32 accumulate          [rows][V]    (hipBLASLt, "TN")
 //   KL rows against the teacher, coef = gscale / total: loss, and the
 //   gradient rounded to half as it is stored: dl    [rows][V]    (row_loss_kernel)
 //   dx[r0:r1] = dl . W / gscale, float32 accumulate [rows][hs]   (hipBLASLt, "NN")
+// The teacher side (head_topk) stops after the logits product: the top-k
+// rows kernel picks each row's k ids and their renormalised probabilities.
 // "half" is the head's type, f16 or bf16, rounded to nearest even.  The two
 // products are plain GEMMs on the matrix cores and go to hipBLASLt; the row
 // work between them is this library's own kernels.  The page slices the
@@ -305,6 +308,43 @@ bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int
 size_t head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
 {
     return head_layout(chunk, V, hs).total;
+}
+
+size_t head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
+{
+    // the same layout without the half-precision gradient
+    const HeadLayout L = head_layout(chunk, V, hs);
+    return L.total - (L.ws - L.dl);
+}
+
+// The teacher side (cortiq-engine train_head.rs, host fn topk): per chunk
+// of rows, act = half(x), logits = act . W^T in float32, then the top-k
+// rows kernel on those logits writes ids and renormalised probabilities.
+int head_topk(const HeadTopkArgs &a, hipStream_t st)
+{
+    hipblasLtHandle_t h = lt_handle();
+    if (!h)
+        return VL_ELAUNCH;
+    const bool bf = a.wdtype == VL_BF16;
+    const hipDataType ht = bf ? HIP_R_16BF : HIP_R_16F;
+    const int64_t chunk = a.chunk < a.ntok ? a.chunk : a.ntok;
+    const HeadLayout L = head_layout(chunk, a.V, a.hs);
+    char *base = static_cast<char *>(a.scratch);
+    float *logits = reinterpret_cast<float *>(base + L.logits);
+    void *act = base + L.act;
+    void *ws = base + L.dl;  // no gradient buffer: the workspace follows act
+    for (int64_t r0 = 0; r0 < a.ntok; r0 += chunk) {
+        const int64_t rows = a.ntok - r0 < chunk ? a.ntok - r0 : chunk;
+        if (to_half(bf, a.x + r0 * a.hs, act, rows * a.hs, st) != hipSuccess)
+            return VL_ELAUNCH;
+        if (!gemm(h, HIPBLAS_OP_T, HIPBLAS_OP_N, a.V, rows, a.hs, 1.f, a.w, a.hs, act, a.hs,
+                  logits, a.V, ht, ws, kHeadWorkspace, st))
+            return VL_ELAUNCH;
+        TopkArgs t{logits, rows, a.V, a.k, a.ids + r0 * a.k, a.probs + r0 * a.k};
+        if (launch_topk(kF32, t, st) != hipSuccess)
+            return VL_ELAUNCH;
+    }
+    return VL_OK;
 }
 
 int head_kl(const HeadArgs &a, hipStream_t st)

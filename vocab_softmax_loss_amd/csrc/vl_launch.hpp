@@ -225,6 +225,19 @@ size_t head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
 // Returns a VL_ status.
 int head_kl(const HeadArgs &a, hipStream_t stream);
 
+// One call of the teacher-side head (checked by the caller).
+struct HeadTopkArgs {
+    const float *x;         // [ntok][hs] hidden rows
+    const void *w;          // [V][hs] head weights, wdtype
+    int wdtype;             // VL_F16 or VL_BF16
+    int64_t ntok, V, hs, k, chunk;
+    uint32_t *ids;          // [ntok][k]
+    float *probs;           // [ntok][k]
+    void *scratch;          // head_topk_scratch_bytes(min(chunk, ntok), V, hs) bytes
+};
+size_t head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
+int head_topk(const HeadTopkArgs &a, hipStream_t stream);
+
 // Each returns hipSuccess or the HIP error of the launch.
 // out = 0: the gradient is written over the logits; out = 1 / 2: float32 KL
 // rows write it rounded to bf16 / f16 into a.gout and leave the logits.
