@@ -120,7 +120,8 @@ __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+// The lanes where p holds: one compare straight into a scalar lane mask.
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // Number of set bits of `mask` in lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t mask)
