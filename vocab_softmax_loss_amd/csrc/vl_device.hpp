@@ -264,11 +264,14 @@ struct RowIO<kBF16, true> {
             x[2 * i + 1] = __builtin_bit_cast(float, r[i] & 0xFFFF0000u);
         }
     }
+    // Non-temporal, as for float32: 16384 x 151936 KL 2.06 -> 1.98 ms, and
+    // the next kernel no longer pays the write-back of dirty lines (the
+    // slice accumulate after that KL 56 -> 39 us).
     __device__ static void store(void *row, uint32_t v, const float (&g)[N])
     {
         f32x8 f = {g[0], g[1], g[2], g[3], g[4], g[5], g[6], g[7]};
         bf16x8 b = __builtin_convertvector(f, bf16x8);
-        reinterpret_cast<bf16x8 *>(row)[v] = b;
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, b), reinterpret_cast<u32x4 *>(row) + v);
     }
     __device__ static void store_elem(void *row, uint32_t j, float g)
     {
@@ -349,6 +352,41 @@ __device__ __forceinline__ typename RowIO<DT, VEC>::Raw neg_inf_raw()
     }
     return r;
 }
+
+// Gradient rows rounded to bf16 (BF) or f16 as they are stored, into a
+// separate half-precision row that a GEMM reads next: N values of float32
+// vector vi of the row at q (non-temporal: written once, read by the next
+// kernel from HBM anyway).
+template <bool BF, int N>
+__device__ __forceinline__ void half_store(char *q, uint32_t vi, const float (&g)[N])
+{
+    if constexpr (N == 4) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        const f32x4 f = {g[0], g[1], g[2], g[3]};
+        unsigned long long bits;
+        if constexpr (BF)
+            bits = __builtin_bit_cast(unsigned long long, __builtin_convertvector(f, bf16x4));
+        else
+            bits = __builtin_bit_cast(unsigned long long, __builtin_convertvector(f, f16x4));
+        __builtin_nontemporal_store(bits, reinterpret_cast<unsigned long long *>(q) + vi);
+    } else if constexpr (N == 8) {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        const f32x8 f = {g[0], g[1], g[2], g[3], g[4], g[5], g[6], g[7]};
+        u32x4 bits;
+        if constexpr (BF)
+            bits = __builtin_bit_cast(u32x4, __builtin_convertvector(f, bf16x8));
+        else
+            bits = __builtin_bit_cast(u32x4, __builtin_convertvector(f, f16x8));
+        __builtin_nontemporal_store(bits, reinterpret_cast<u32x4 *>(q) + vi);
+    } else {
+        if constexpr (BF)
+            reinterpret_cast<__bf16 *>(q)[vi] = (__bf16)g[0];
+        else
+            reinterpret_cast<_Float16 *>(q)[vi] = (_Float16)g[0];
+    }
+}
+
 
 template <int DT>
 __device__ __forceinline__ size_t elt_bytes()

@@ -77,36 +77,6 @@ constexpr int online_unroll(int hk = 0)
 // Where the gradient goes: over the logits (OUT = 0), or, rounded to bf16
 // (OUT = 1) or f16 (OUT = 2), into a separate row-major [ntok][V] buffer
 // that the next step reads as a GEMM operand.
-template <bool BF, int N>
-__device__ __forceinline__ void half_store(char *q, uint32_t vi, const float (&g)[N])
-{
-    if constexpr (N == 4) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-        const f32x4 f = {g[0], g[1], g[2], g[3]};
-        unsigned long long bits;
-        if constexpr (BF)
-            bits = __builtin_bit_cast(unsigned long long, __builtin_convertvector(f, bf16x4));
-        else
-            bits = __builtin_bit_cast(unsigned long long, __builtin_convertvector(f, f16x4));
-        __builtin_nontemporal_store(bits, reinterpret_cast<unsigned long long *>(q) + vi);
-    } else if constexpr (N == 8) {
-        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-        const f32x8 f = {g[0], g[1], g[2], g[3], g[4], g[5], g[6], g[7]};
-        u32x4 bits;
-        if constexpr (BF)
-            bits = __builtin_bit_cast(u32x4, __builtin_convertvector(f, bf16x8));
-        else
-            bits = __builtin_bit_cast(u32x4, __builtin_convertvector(f, f16x8));
-        __builtin_nontemporal_store(bits, reinterpret_cast<u32x4 *>(q) + vi);
-    } else {
-        if constexpr (BF)
-            reinterpret_cast<__bf16 *>(q)[vi] = (__bf16)g[0];
-        else
-            reinterpret_cast<_Float16 *>(q)[vi] = (_Float16)g[0];
-    }
-}
-
 template <int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF, bool RL, int HK, int OUT>
 struct RowKernel {
     using IO = RowIO<DT, VEC>;

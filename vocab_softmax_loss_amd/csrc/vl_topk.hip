@@ -592,8 +592,13 @@ hipError_t launch_cap(const TopkArgs &a, hipStream_t st)
 template <int DT, bool VEC>
 hipError_t launch_dt(const TopkArgs &a, hipStream_t st)
 {
+    // The buffer holds k kept entries and one sub-tile, and after each
+    // compaction it needs room for a few more sub-tiles' candidates, or it
+    // compacts on every sub-tile that holds one: at least half of max(k,
+    // sub-tile) spare.  (float32 k = 256 at V = 151936 in 512 entries, with
+    // no spare: 5.6 ms; in 1024: see the design notes.)
     constexpr int SUB = kWave * RowIO<DT, VEC>::N;
-    const int64_t need = a.k + SUB;
+    const int64_t need = a.k + SUB + (a.k > SUB ? a.k : SUB) / 2;
     if (need <= 512)
         return launch_cap<DT, VEC, 512>(a, st);
     if (need <= 1024)
