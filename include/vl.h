@@ -187,7 +187,9 @@ size_t vl_split_workspace_bytes(void);
  * sums are taken in another order).  The split runs as one cooperative
  * launch, so all its workgroups are resident together; should a part's
  * partners still fail to answer within about a second, that row's loss,
- * lse and gradient come out NaN and the call completes.
+ * lse and gradient come out NaN and the call completes.  On a stream under
+ * capture the rows are not split (a cooperative launch is not captured):
+ * the call runs vl_ce_fwd_bwd's / vl_kl_fwd_bwd's kernels.
  */
 int vl_ce_fwd_bwd_ws(void *logits, int dtype, const uint32_t *labels, float *loss, float *lse,
                      int64_t ntok, int64_t V, const vl_range *rng, float scale, void *workspace,

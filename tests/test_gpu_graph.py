@@ -99,3 +99,48 @@ def test_graph_replays_match_eager(vl):
         # eager work of the program's own between replays
         step()
         torch.cuda.synchronize()
+
+
+def test_split_calls_under_capture_run_whole_rows(vl):
+    """The workspace and no-allocation calls inside a captured graph: a
+    split is one cooperative launch, which a capture does not take, so they
+    run the rows whole -- every replay gives the unsplit call's bits."""
+    n, V, k = 96, 128256, 64
+    src = gi.normal_logits(n, V, 2.0, 8101, DEV)
+    ids = gi.distinct_ids(n, V, k, 8102, DEV)
+    probs = gi.softmax_probs(n, k, 1.5, 8103, DEV)
+    ws = torch.empty(vl.vl_split_workspace_bytes(), dtype=torch.uint8, device=DEV)
+    ref = src.clone()
+    ref_loss = torch.empty(n, device=DEV)
+    vl.vl_kl_fwd_bwd(ref, ids, probs, ref_loss, coef=1.0 / n)
+    a, b = torch.empty_like(src), torch.empty_like(src)
+    la, lb = torch.empty(n, device=DEV), torch.empty(n, device=DEV)
+
+    def step():
+        vl.vl_kl_fwd_bwd_ws(a, ids, probs, la, ws, coef=1.0 / n)
+        vl.vl_kl_fwd_bwd_noalloc(b, ids, probs, lb, coef=1.0 / n)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        a.copy_(src)
+        b.copy_(src)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    a.copy_(src)
+    b.copy_(src)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        la.zero_()
+        lb.zero_()
+        a.copy_(src)
+        b.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, lt in ((a, la), (b, lb)):
+            assert torch.equal(t, ref) and torch.equal(lt, ref_loss), f"replay {rep}"
+        step()  # eager, split, between replays
+        torch.cuda.synchronize()

@@ -147,10 +147,15 @@ namespace {
 // 19456 vectors (155648 values) a 1024-thread block holds in registers.  The
 // bf16 rows in between run as fast whole in one block's registers (16384 x
 // 151936: 2.06 ms either way) and need no exchange.
-bool use_split(int dtype, const vl::RowArgs &a, int &S)
+// A split is one cooperative launch, which a stream under capture does not
+// take: captured calls run the rows whole (the same results within rounding).
+bool use_split(int dtype, const vl::RowArgs &a, int &S, hipStream_t stream)
 {
     const int N = dtype == VL_F32 ? 4 : 8;
     if ((uintptr_t)a.logits % 16 != 0 || a.V % N != 0)
+        return false;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
         return false;
     const int64_t nvec = a.V / N;
     if (nvec <= (dtype == VL_F32 ? 8192 : 19456))
@@ -163,7 +168,7 @@ int rows_ws(int dtype, bool kl, const vl::RowArgs &a, void *ws, size_t ws_bytes,
             hipStream_t stream)
 {
     int S = 0;
-    if (use_split(dtype, a, S))
+    if (use_split(dtype, a, S, stream))
         return status_of(vl::launch_rows_split(dtype, kl, a, S, ws, ws_bytes, stream));
     return status_of(vl::launch_rows(dtype, kl, a, stream));
 }
@@ -234,7 +239,7 @@ int vl_kl_fwd_bwd_noalloc(void *logits, int dtype, const uint32_t *ids, const fl
     a.lse = lse;
     a.coef = coef;
     int S = 0;
-    if (!use_split(dtype, a, S))
+    if (!use_split(dtype, a, S, stream))
         return status_of(vl::launch_rows(dtype, true, a, stream));
     void *ws = nullptr;
     if (vl::split_scratch(&ws) != hipSuccess)
