@@ -158,8 +158,14 @@ def test_head_scratch_bytes(lib):
     f = lib.vl_head_scratch_bytes
     a = 256
     up = lambda b: (b + a - 1) // a * a  # noqa: E731
-    want = up(32 * 1024 * 4) + up(32 * 256 * 2) + up(32 * 1024 * 2) + (64 << 20)
+    # logits, half hidden rows (hs padded to 64), half gradient, (max, sum)
+    # records per 128 columns, lse, loss sums per 2048 columns, workspace
+    want = (up(32 * 1024 * 4) + up(32 * 256 * 2) + up(32 * 1024 * 2) + up(32 * 8 * 8)
+            + up(32 * 4) + up(32 * 1 * 4) + (64 << 20))
     assert f(32, 1024, 256) == want
+    want = (up(5 * 1000 * 4) + up(5 * 128 * 2) + up(5 * 1000 * 2) + up(5 * 8 * 8)
+            + up(5 * 4) + up(5 * 1 * 4) + (64 << 20))
+    assert f(5, 1000, 72) == want
     assert f(0, 1024, 256) == 0 and f(32, 0, 256) == 0 and f(32, 1024, 0) == 0
     assert f(32, (1 << 19) + 1, 256) == 0
 

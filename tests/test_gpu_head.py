@@ -89,6 +89,10 @@ def test_head_page_case(vl):
     (33, 4096, 256, 64, 33),     # one chunk
     (70, 32000, 512, 64, 64),    # language-model vocabulary, two chunks
     (5, 151936, 128, 256, 4),    # the largest vocabulary, ragged
+    (300, 2048, 128, 16, 300),   # two 256-row tiles of the product, the second ragged
+    (9, 4096, 64, 300, 9),       # k above 256: the gradient pass reads the ids twice
+    (7, 999, 64, 5, 4),          # V not a multiple of 4: the element path of the gradient
+    (6, 500, 20, 4, 3),          # hs not a multiple of 8: hipBLASLt and the fused row kernel
 ])
 def test_head_shapes(vl, dtype, ntok, V, hs, k, chunk):
     c = gi.head_inputs(ntok, V, hs, k, 3000 + V + hs, DEV, HALF[dtype])
@@ -111,6 +115,29 @@ def test_head_zero_rows_and_repeat(vl):
     b = run_head(vl, c["x"], c["w"], c["ids"], c["probs"], 20, 64.0, 8)
     np.testing.assert_allclose(a[0], b[0], rtol=1e-6, atol=0)
     np.testing.assert_allclose(a[1], b[1], rtol=1e-6, atol=1e-12)
+
+
+def test_head_bad_id_and_padded_teacher(vl):
+    """An id >= V with p > 0 makes that row's loss NaN and leaves the other
+    rows as the oracle has them; a teacher list padded with a repeated id at
+    probability 0 gives the oracle's result (those entries take no part)."""
+    ntok, V, hs, k = 12, 3000, 64, 8
+    c = gi.head_inputs(ntok, V, hs, k, 3200, DEV, torch.bfloat16)
+    ids, probs = c["ids"].clone(), c["probs"].clone()
+    ids[3, 2] = V          # out of range, p > 0
+    ids[5, 6:] = ids[5, 0]  # padding: repeated id at probability 0
+    probs[5, 6:] = 0.0
+    total, gscale = ntok, 64.0
+    loss, dx = run_head(vl, c["x"], c["w"], ids, probs, total, gscale, 8)
+    assert np.isnan(loss[3])
+    keep = [r for r in range(ntok) if r != 3]
+    ids_ok = ids.clone()
+    ids_ok[3, 2] = 0
+    rl, rdx = oracle_for(c["x"], c["w"], ids_ok, probs, total, gscale, "bf16")
+    assert np.isfinite(loss[keep]).all()
+    assert (np.abs(loss[keep] - rl[keep]) <= 1e-4 + 1e-5 * np.abs(rl[keep])).all()
+    for t in keep:
+        assert rel_l2(dx[t], rdx[t]) < DX_TOL["bf16"], t
 
 
 # ------------------------------------------------ the teacher side (vl_head_topk)

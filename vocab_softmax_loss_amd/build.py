@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libvl.so")
 ARCH = os.environ.get("VL_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["vl_api.cpp", "vl_rows.hip", "vl_ce_split.hip", "vl_topk.hip", "vl_acc.hip",
-           "vl_head.hip", "vl_slice.hip", "vl_split.hip"]
+           "vl_head.hip", "vl_slice.hip", "vl_split.hip", "vl_gemm.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

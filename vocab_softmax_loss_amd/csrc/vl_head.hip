@@ -1,18 +1,22 @@
 // Vocabulary head for gfx950 (cortiq-engine train_head.rs: Head,
 // HeadScratch, head_kl, topk).  The student side with the distillation KL,
 // for each chunk of rows:
-//   act    = half(x[r0:r1])                         [rows][hs]   (to_half_kernel)
-//   logits = act . W^T, float32 accumulate          [rows][V]    (hipBLASLt, "TN")
-//   KL rows against the teacher, coef = gscale / total: loss, and the
-//   gradient rounded to half as it is stored: dl    [rows][V]    (row_loss_kernel)
+//   act    = half(x[r0:r1]), rows padded to lda     [rows][lda]  (to_half_rows_kernel)
+//   logits = act . W^T, float32 accumulate, with    [rows][V]    (logits_kernel,
+//            (max, sum exp) per row and 128 columns [rows][R]     matrix cores)
+//   lse from those records                          [rows]       (head_lse_kernel)
+//   gradient coef (softmax - t), coef = gscale / total, rounded to half as it
+//   is stored, and the loss terms per chunk         [rows][V]    (head_grad_kernel)
+//   loss = the KL of each row                       [rows]       (head_loss_kernel)
 //   dx[r0:r1] = dl . W / gscale, float32 accumulate [rows][hs]   (hipBLASLt, "NN")
 // The teacher side (head_topk) stops after the logits product: the top-k
 // rows kernel picks each row's k ids and their renormalised probabilities.
-// "half" is the head's type, f16 or bf16, rounded to nearest even.  The two
-// products are plain GEMMs on the matrix cores and go to hipBLASLt; the row
-// work between them is this library's own kernels.  The page slices the
-// head into vocabulary planes because a WebGPU storage binding stops at
-// 2 GiB; HIP has no such limit, so each product spans the whole vocabulary.
+// "half" is the head's type, f16 or bf16, rounded to nearest even.  Heads
+// whose rows are not whole 16-byte vectors run the logits product in
+// hipBLASLt and the fused KL row kernel (row_loss_kernel) instead.  The
+// page slices the head into vocabulary planes because a WebGPU storage
+// binding stops at 2 GiB; HIP has no such limit, so each product spans the
+// whole vocabulary.
 #include <hipblaslt/hipblaslt.h>
 #include <math.h>
 
@@ -56,6 +60,227 @@ __global__ __launch_bounds__(256) void to_half_kernel(const float *src, void *ds
     }
 }
 
+// dst row r = half(src row r) in columns [0, hs), zero in [hs, lda): the
+// hidden rows as the matrix-core product's A operand, each row padded to a
+// whole number of its 64-column K steps.  8 columns per thread; hs is a
+// multiple of 8 and src 16-byte aligned (the caller checks).
+template <bool BF>
+__global__ __launch_bounds__(256) void to_half_rows_kernel(const float *src, void *dst,
+                                                           int64_t rows, int64_t hs, int64_t lda)
+{
+    const int64_t per_row = lda / 8, n = rows * per_row;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const int64_t r = i / per_row, j = (i - r * per_row) * 8;
+        f32x8 f = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (j < hs) {
+            const f32x4 *s4 = reinterpret_cast<const f32x4 *>(src + r * hs + j);
+            const f32x4 a = __builtin_nontemporal_load(s4);
+            const f32x4 b = __builtin_nontemporal_load(s4 + 1);
+            f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        }
+        if constexpr (BF)
+            reinterpret_cast<bf16x8 *>(dst)[i] = __builtin_convertvector(f, bf16x8);
+        else
+            reinterpret_cast<f16x8 *>(dst)[i] = __builtin_convertvector(f, f16x8);
+    }
+}
+
+namespace {
+
+__device__ __forceinline__ float head_scalar_f32(const float *p, int64_t i)
+{
+    return ((const __attribute__((address_space(4))) float *)p)[i];
+}
+
+}  // namespace
+
+// The row's log-sum-exp from the product's (max, sum exp) records, one wave
+// per row: lse = M + ln sum_t z_t exp(a_t - M), M the largest anchor; empty
+// records (z = 0, anchor -inf) are left out.
+__global__ __launch_bounds__(256) void head_lse_kernel(const float2 *rec, int64_t nrec,
+                                                       int64_t rows, float *lse)
+{
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int lane = lane_id();
+    const float2 *rr = rec + row * nrec;
+    float m = -INFINITY;
+    for (int64_t q = lane; q < nrec; q += kWave) {
+        const float2 t = rr[q];
+        m = t.y > 0.f ? fmaxf(m, t.x) : m;
+    }
+    const float M = wave_max(m);
+    float z = 0.f;
+    for (int64_t q = lane; q < nrec; q += kWave) {
+        const float2 t = rr[q];
+        z += t.y > 0.f ? t.y * __expf(t.x - M) : 0.f;
+    }
+    const float Z = wave_sum(z);
+    if (lane == 0)
+        lse[row] = M + __logf(Z);
+}
+
+// One call of the head's gradient pass (checked by the caller).
+struct HeadGradArgs {
+    const float *logits;     // [rows][V] float32
+    float *lse;              // [rows], written by the lse pass
+    const uint32_t *ids;     // [rows][k]
+    const float *probs;      // [rows][k]
+    void *dl;                // [rows][V] half-precision gradient, written
+    float *part;             // [rows][cpr] loss terms summed per chunk, written
+    float *loss;             // [rows], written by the loss pass
+    int64_t rows, V, k;
+    float coef;
+};
+
+constexpr int kHeadGradBlock = 512;
+constexpr int kHeadGradVecs = 4;  // 16-byte vectors (or elements) per lane
+
+// dl = half(coef (exp(s - lse) - t)) over the float32 logits, element-wise:
+// workgroup (row, chunk) covers 512 threads x 4 vectors of the row; wave w
+// owns 256 consecutive vectors, lane l those at l + 64 u.  The row's teacher
+// ids are read 4 per lane; a ballot finds those inside the wave's span, and
+// for each the lane owning its vector subtracts p before the single store
+// and forms the entry's loss term p (ln p - s + lse) (p > 0 only: entries
+// with probability 0 take no part).  The terms of the chunk are summed in
+// a fixed order (per wave in id order, then wave by wave) into part.
+template <bool BF, bool VEC>
+__global__ __launch_bounds__(kHeadGradBlock) void head_grad_kernel(HeadGradArgs a, int64_t cpr)
+{
+    constexpr int N = VEC ? 4 : 1;
+    constexpr int UV = kHeadGradVecs;
+    using IO = RowIO<kF32, VEC>;
+    __shared__ float sh_part[kHeadGradBlock / kWave];
+    const uint32_t tid = threadIdx.x;
+    const int lane = lane_id();
+    const uint32_t wid = tid / kWave;
+    const int64_t row = blockIdx.x / cpr;
+    const uint32_t chunk = (uint32_t)(blockIdx.x - row * cpr);
+    const uint32_t nvec = (uint32_t)(a.V / N);
+    const uint32_t vw = chunk * kHeadGradBlock * UV + (tid - (uint32_t)lane) * UV;
+    const char *p = reinterpret_cast<const char *>(a.logits) + row * a.V * 4;
+    char *q = reinterpret_cast<char *>(a.dl) + row * a.V * 2;
+    const float L = head_scalar_f32(a.lse, row);
+    const uint32_t *idr = a.ids + row * a.k;
+    const float *pr = a.probs + row * a.k;
+    const int64_t lo = (int64_t)vw * N;
+    const int64_t rest = a.V - lo;
+    const int64_t hi = lo + ((int64_t)kWave * UV * N < rest ? (int64_t)kWave * UV * N : rest);
+    const bool v4 = (a.k % 4 == 0) && ((uintptr_t)idr % 16 == 0);
+    uint32_t id[4];
+    // lane l holds teacher entries q0 + 4 l .. q0 + 4 l + 3
+    auto load_ids = [&](int64_t q0) {
+        if (v4) {
+            const int64_t qq = q0 + 4 * lane;
+            if (qq < a.k) {
+                const u32x4 t = *reinterpret_cast<const u32x4 *>(idr + qq);
+                id[0] = t[0];
+                id[1] = t[1];
+                id[2] = t[2];
+                id[3] = t[3];
+            } else {
+                id[0] = id[1] = id[2] = id[3] = 0xFFFFFFFFu;
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int64_t qq = q0 + 4 * lane + b;
+                id[b] = qq < a.k ? idr[qq] : 0xFFFFFFFFu;
+            }
+        }
+    };
+    load_ids(0);
+    float x[UV][N], g[UV][N];
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+        const uint32_t v = vw + (uint32_t)u * kWave + (uint32_t)lane;
+        IO::unpack(IO::load_stream(p, v < nvec ? v : nvec - 1), x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UV; ++u)
+#pragma unroll
+        for (int e = 0; e < N; ++e)
+            g[u][e] = __expf(x[u][e] - L);
+    float part = 0.f;  // wave-uniform
+    for (int64_t q0 = 0; q0 < a.k; q0 += 4 * kWave) {
+        if (q0 > 0)
+            load_ids(q0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            uint64_t mask = ballot((int64_t)id[b] >= lo && (int64_t)id[b] < hi);
+            while (mask) {
+                const int src = __builtin_ctzll(mask);
+                mask &= mask - 1;
+                const uint32_t jj =
+                    (uint32_t)((int64_t)__builtin_amdgcn_readlane((int)id[b], src) - lo);
+                const float pv = head_scalar_f32(pr, q0 + 4 * src + b);
+                const uint32_t jv = jj / N, je = jj % N;
+                const int owner = (int)(jv % kWave);
+                float term = 0.f;
+#pragma unroll
+                for (int u = 0; u < UV; ++u) {
+                    if (jv == (uint32_t)(u * kWave + lane)) {
+#pragma unroll
+                        for (int e = 0; e < N; ++e)
+                            if (je == (uint32_t)e) {
+                                g[u][e] -= pv;
+                                term = pv > 0.f ? pv * (__logf(pv) - x[u][e] + L) : 0.f;
+                            }
+                    }
+                }
+                part += __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, term), owner));
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+        const uint32_t v = vw + (uint32_t)u * kWave + (uint32_t)lane;
+        if (v < nvec) {
+#pragma unroll
+            for (int e = 0; e < N; ++e)
+                g[u][e] *= a.coef;
+            half_store<BF, N>(q, v, g[u]);
+        }
+    }
+    if (lane == 0)
+        sh_part[wid] = part;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < kHeadGradBlock / kWave; ++i)
+            s += sh_part[i];
+        a.part[row * cpr + chunk] = s;
+    }
+}
+
+// loss[row] = the row's chunk sums in order; NaN when an entry with p > 0
+// names an id >= V (no chunk saw it).  One wave per row.
+__global__ __launch_bounds__(256) void head_loss_kernel(const float *part, int64_t cpr,
+                                                        const uint32_t *ids, const float *probs,
+                                                        int64_t k, int64_t V, int64_t rows,
+                                                        float *loss)
+{
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int lane = lane_id();
+    bool bad = false;
+    for (int64_t q = lane; q < k; q += kWave)
+        bad |= probs[row * k + q] > 0.f && (int64_t)ids[row * k + q] >= V;
+    float s = 0.f;
+    if (lane == 0)
+        for (int64_t c = 0; c < cpr; ++c)
+            s += part[row * cpr + c];
+    if (ballot(bad) != 0ull)
+        s = NAN;
+    if (lane == 0)
+        loss[row] = s;
+}
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -63,18 +288,39 @@ constexpr size_t kHeadWorkspace = size_t(64) << 20;  // hipBLASLt workspace
 
 size_t align_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 
+// Scratch of one chunk of rows, each region 256-byte aligned:
+//   logits [chunk][V] float32, act [chunk][lda] half (lda = hs rounded up to
+//   64), dl [chunk][V] half (student side only), rec [chunk][2 ceil(V/256)]
+//   (max, sum) pairs, lse [chunk], part [chunk][ceil(V/2048)] loss sums
+//   (student side only), then the hipBLASLt workspace.
 struct HeadLayout {
-    size_t logits, act, dl, ws, total;
+    size_t logits, act, dl, rec, lse, part, ws, total;
 };
 
-HeadLayout head_layout(int64_t chunk, int64_t V, int64_t hs)
+int64_t head_lda(int64_t hs) { return (hs + kLogitsKStep - 1) / kLogitsKStep * kLogitsKStep; }
+int64_t head_nrec(int64_t V) { return 2 * ((V + kLogitsTile - 1) / kLogitsTile); }
+int64_t head_cpr_max(int64_t V)
+{
+    return (V + kHeadGradBlock * kHeadGradVecs - 1) / (kHeadGradBlock * kHeadGradVecs);
+}
+
+HeadLayout head_layout(int64_t chunk, int64_t V, int64_t hs, bool student)
 {
     HeadLayout L{};
-    L.logits = 0;
-    L.act = align_up((size_t)chunk * (size_t)V * 4);
-    L.dl = L.act + align_up((size_t)chunk * (size_t)hs * 2);
-    L.ws = L.dl + align_up((size_t)chunk * (size_t)V * 2);
-    L.total = L.ws + kHeadWorkspace;
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        const size_t here = at;
+        at += align_up(bytes);
+        return here;
+    };
+    L.logits = take((size_t)chunk * (size_t)V * 4);
+    L.act = take((size_t)chunk * (size_t)head_lda(hs) * 2);
+    L.dl = student ? take((size_t)chunk * (size_t)V * 2) : at;
+    L.rec = take((size_t)chunk * (size_t)head_nrec(V) * 8);
+    L.lse = take((size_t)chunk * 4);
+    L.part = student ? take((size_t)chunk * (size_t)head_cpr_max(V) * 4) : at;
+    L.ws = at;
+    L.total = at + kHeadWorkspace;
     return L;
 }
 
@@ -307,39 +553,124 @@ bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int
 
 size_t head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
 {
-    return head_layout(chunk, V, hs).total;
+    return head_layout(chunk, V, hs, true).total;
 }
 
 size_t head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
 {
-    // the same layout without the half-precision gradient
-    const HeadLayout L = head_layout(chunk, V, hs);
-    return L.total - (L.ws - L.dl);
+    return head_layout(chunk, V, hs, false).total;
 }
+
+namespace {
+
+// The product runs on this library's matrix-core kernel when the head's
+// rows are whole 16-byte vectors (hs a multiple of 8, w 16-byte aligned)
+// and the hidden rows are 16-byte aligned; otherwise in hipBLASLt.
+bool own_product(const float *x, const void *w, int64_t hs)
+{
+    return hs % 8 == 0 && (uintptr_t)w % 16 == 0 && (uintptr_t)x % 16 == 0;
+}
+
+hipError_t to_half_rows(bool bf, const float *src, void *dst, int64_t rows, int64_t hs,
+                        int64_t lda, hipStream_t st)
+{
+    const int64_t n = rows * (lda / 8);
+    int64_t grid = (n + 255) / 256;
+    const int64_t cap = (int64_t)device_cus() * 8;
+    if (grid > cap)
+        grid = cap;
+    if (grid < 1)
+        grid = 1;
+    if (bf)
+        hipLaunchKernelGGL((to_half_rows_kernel<true>), dim3((unsigned)grid), dim3(256), 0, st,
+                           src, dst, rows, hs, lda);
+    else
+        hipLaunchKernelGGL((to_half_rows_kernel<false>), dim3((unsigned)grid), dim3(256), 0, st,
+                           src, dst, rows, hs, lda);
+    return hipGetLastError();
+}
+
+// The KL rows of one chunk from the product's records: lse, then the
+// half-precision gradient with the chunk sums of the loss terms, then the
+// loss.
+hipError_t head_kl_rows(bool bf, const HeadGradArgs &h, const float2 *rec, int64_t nrec,
+                        hipStream_t st)
+{
+    const unsigned rgrid = (unsigned)((h.rows + 3) / 4);
+    hipLaunchKernelGGL(head_lse_kernel, dim3(rgrid), dim3(256), 0, st, rec, nrec, h.rows,
+                       h.lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const bool vec = h.V % 4 == 0;
+    const int64_t span = (int64_t)kHeadGradBlock * kHeadGradVecs * (vec ? 4 : 1);
+    const int64_t cpr = (h.V + span - 1) / span;
+    const int64_t grid = h.rows * cpr;
+    if (grid > INT32_MAX)
+        return hipErrorInvalidConfiguration;
+    const dim3 gd((unsigned)grid), bd(kHeadGradBlock);
+    if (bf) {
+        if (vec)
+            hipLaunchKernelGGL((head_grad_kernel<true, true>), gd, bd, 0, st, h, cpr);
+        else
+            hipLaunchKernelGGL((head_grad_kernel<true, false>), gd, bd, 0, st, h, cpr);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((head_grad_kernel<false, true>), gd, bd, 0, st, h, cpr);
+        else
+            hipLaunchKernelGGL((head_grad_kernel<false, false>), gd, bd, 0, st, h, cpr);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(head_loss_kernel, dim3(rgrid), dim3(256), 0, st, h.part, cpr, h.ids,
+                       h.probs, h.k, h.V, h.rows, h.loss);
+    return hipGetLastError();
+}
+
+}  // namespace
 
 // The teacher side (cortiq-engine train_head.rs, host fn topk): per chunk
 // of rows, act = half(x), logits = act . W^T in float32, then the top-k
 // rows kernel on those logits writes ids and renormalised probabilities.
 int head_topk(const HeadTopkArgs &a, hipStream_t st)
 {
-    hipblasLtHandle_t h = lt_handle();
-    if (!h)
-        return VL_ELAUNCH;
     const bool bf = a.wdtype == VL_BF16;
+    const bool own = own_product(a.x, a.w, a.hs);
+    hipblasLtHandle_t h = nullptr;
+    if (!own && !(h = lt_handle()))
+        return VL_ELAUNCH;
     const hipDataType ht = bf ? HIP_R_16BF : HIP_R_16F;
     const int64_t chunk = a.chunk < a.ntok ? a.chunk : a.ntok;
-    const HeadLayout L = head_layout(chunk, a.V, a.hs);
+    const HeadLayout L = head_layout(chunk, a.V, a.hs, false);
     char *base = static_cast<char *>(a.scratch);
     float *logits = reinterpret_cast<float *>(base + L.logits);
     void *act = base + L.act;
-    void *ws = base + L.dl;  // no gradient buffer: the workspace follows act
+    void *ws = base + L.ws;
+    const int64_t lda = head_lda(a.hs);
     for (int64_t r0 = 0; r0 < a.ntok; r0 += chunk) {
         const int64_t rows = a.ntok - r0 < chunk ? a.ntok - r0 : chunk;
-        if (to_half(bf, a.x + r0 * a.hs, act, rows * a.hs, st) != hipSuccess)
-            return VL_ELAUNCH;
-        if (!gemm(h, HIPBLAS_OP_T, HIPBLAS_OP_N, a.V, rows, a.hs, 1.f, a.w, a.hs, act, a.hs,
-                  logits, a.V, ht, ws, kHeadWorkspace, st))
-            return VL_ELAUNCH;
+        if (own) {
+            if (to_half_rows(bf, a.x + r0 * a.hs, act, rows, a.hs, lda, st) != hipSuccess)
+                return VL_ELAUNCH;
+            LogitsArgs g{};
+            g.a = act;
+            g.b = a.w;
+            g.c = logits;
+            g.M = rows;
+            g.N = a.V;
+            g.K = a.hs;
+            g.lda = lda;
+            g.ldc = a.V;
+            if (launch_logits(bf, false, g, st) != hipSuccess)
+                return VL_ELAUNCH;
+        } else {
+            if (to_half(bf, a.x + r0 * a.hs, act, rows * a.hs, st) != hipSuccess)
+                return VL_ELAUNCH;
+            if (!gemm(h, HIPBLAS_OP_T, HIPBLAS_OP_N, a.V, rows, a.hs, 1.f, a.w, a.hs, act, a.hs,
+                      logits, a.V, ht, ws, kHeadWorkspace, st))
+                return VL_ELAUNCH;
+        }
         TopkArgs t{logits, rows, a.V, a.k, a.ids + r0 * a.k, a.probs + r0 * a.k};
         if (launch_topk(kF32, t, st) != hipSuccess)
             return VL_ELAUNCH;
@@ -347,42 +678,86 @@ int head_topk(const HeadTopkArgs &a, hipStream_t st)
     return VL_OK;
 }
 
+// The student side (cortiq-engine train_head.rs, head_kl): per chunk of
+// rows, act = half(x); logits = act . W^T with the per-row statistics of
+// every 128 columns (this library's matrix-core product); the KL rows from
+// those statistics (lse, then the gradient rounded to half straight into
+// the next product's operand, with the loss terms, then the loss); and
+// dx = dl . W / gscale in hipBLASLt.  Heads the matrix-core product does
+// not take (hs not a multiple of 8, unaligned rows) run the logits product
+// in hipBLASLt and the fused KL row kernel.
 int head_kl(const HeadArgs &a, hipStream_t st)
 {
     hipblasLtHandle_t h = lt_handle();
     if (!h)
         return VL_ELAUNCH;
     const bool bf = a.wdtype == VL_BF16;
+    const bool own = own_product(a.x, a.w, a.hs);
     const hipDataType ht = bf ? HIP_R_16BF : HIP_R_16F;
     const int64_t chunk = a.chunk < a.ntok ? a.chunk : a.ntok;
-    const HeadLayout L = head_layout(chunk, a.V, a.hs);
+    const HeadLayout L = head_layout(chunk, a.V, a.hs, true);
     char *base = static_cast<char *>(a.scratch);
     float *logits = reinterpret_cast<float *>(base + L.logits);
     void *act = base + L.act;
     void *dl = base + L.dl;
+    float2 *rec = reinterpret_cast<float2 *>(base + L.rec);
+    float *lse = reinterpret_cast<float *>(base + L.lse);
+    float *part = reinterpret_cast<float *>(base + L.part);
     void *ws = base + L.ws;
     const float coef = a.gscale / (float)a.total;
+    const int64_t lda = head_lda(a.hs);
     for (int64_t r0 = 0; r0 < a.ntok; r0 += chunk) {
         const int64_t rows = a.ntok - r0 < chunk ? a.ntok - r0 : chunk;
-        if (to_half(bf, a.x + r0 * a.hs, act, rows * a.hs, st) != hipSuccess)
-            return VL_ELAUNCH;
-        // logits (row-major rows x V) = column-major V x rows = W . act^T
-        if (!gemm(h, HIPBLAS_OP_T, HIPBLAS_OP_N, a.V, rows, a.hs, 1.f, a.w, a.hs, act, a.hs,
-                  logits, a.V, ht, ws, kHeadWorkspace, st))
-            return VL_ELAUNCH;
-        RowArgs r{};
-        r.logits = logits;
-        r.ids = a.ids + r0 * a.k;
-        r.probs = a.probs + r0 * a.k;
-        r.loss = a.loss + r0;
-        r.ntok = rows;
-        r.V = a.V;
-        r.k = a.k;
-        r.walk = make_walk(rows, 0, 0, 0);
-        r.coef = coef;
-        r.gout = dl;  // the gradient goes straight to the GEMM operand, rounded
-        if (launch_rows(kF32, true, r, st, bf ? 1 : 2) != hipSuccess)
-            return VL_ELAUNCH;
+        if (own) {
+            if (to_half_rows(bf, a.x + r0 * a.hs, act, rows, a.hs, lda, st) != hipSuccess)
+                return VL_ELAUNCH;
+            LogitsArgs g{};
+            g.a = act;
+            g.b = a.w;
+            g.c = logits;
+            g.rec = reinterpret_cast<float *>(rec);
+            g.M = rows;
+            g.N = a.V;
+            g.K = a.hs;
+            g.lda = lda;
+            g.ldc = a.V;
+            if (launch_logits(bf, true, g, st) != hipSuccess)
+                return VL_ELAUNCH;
+            HeadGradArgs hg{};
+            hg.logits = logits;
+            hg.lse = lse;
+            hg.ids = a.ids + r0 * a.k;
+            hg.probs = a.probs + r0 * a.k;
+            hg.dl = dl;
+            hg.part = part;
+            hg.loss = a.loss + r0;
+            hg.rows = rows;
+            hg.V = a.V;
+            hg.k = a.k;
+            hg.coef = coef;
+            if (head_kl_rows(bf, hg, rec, head_nrec(a.V), st) != hipSuccess)
+                return VL_ELAUNCH;
+        } else {
+            if (to_half(bf, a.x + r0 * a.hs, act, rows * a.hs, st) != hipSuccess)
+                return VL_ELAUNCH;
+            // logits (row-major rows x V) = column-major V x rows = W . act^T
+            if (!gemm(h, HIPBLAS_OP_T, HIPBLAS_OP_N, a.V, rows, a.hs, 1.f, a.w, a.hs, act, a.hs,
+                      logits, a.V, ht, ws, kHeadWorkspace, st))
+                return VL_ELAUNCH;
+            RowArgs r{};
+            r.logits = logits;
+            r.ids = a.ids + r0 * a.k;
+            r.probs = a.probs + r0 * a.k;
+            r.loss = a.loss + r0;
+            r.ntok = rows;
+            r.V = a.V;
+            r.k = a.k;
+            r.walk = make_walk(rows, 0, 0, 0);
+            r.coef = coef;
+            r.gout = dl;  // the gradient goes straight to the GEMM operand, rounded
+            if (launch_rows(kF32, true, r, st, bf ? 1 : 2) != hipSuccess)
+                return VL_ELAUNCH;
+        }
         // dx (row-major rows x hs) = column-major hs x rows = W^T . dl^T
         if (!gemm(h, HIPBLAS_OP_N, HIPBLAS_OP_N, a.hs, rows, a.V, 1.f / a.gscale, a.w, a.hs, dl,
                   a.V, a.dx + r0 * a.hs, a.hs, ht, ws, kHeadWorkspace, st))

@@ -238,6 +238,20 @@ struct HeadTopkArgs {
 size_t head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
 int head_topk(const HeadTopkArgs &a, hipStream_t stream);
 
+// The head's logits product on the matrix cores, with the per-row
+// statistics of each 128-column half tile (vl_gemm.hip).
+struct LogitsArgs {
+    const void *a;              // [M][lda] half hidden rows; zero in columns [K, lda)
+    const void *b;              // [N][K] half head weights, rows 16-byte aligned
+    float *c;                   // [M][ldc] float32 logits, written
+    float *rec;                 // [M][2 tiles_n] (max, sum exp) pairs, or null
+    int64_t M, N, K, lda, ldc;  // lda a multiple of 64
+    int64_t tiles_m, tiles_n;   // set by the launcher: 256-row and 256-column tiles
+};
+constexpr int64_t kLogitsTile = 256;
+constexpr int64_t kLogitsKStep = 64;
+hipError_t launch_logits(bool bf, bool stats, const LogitsArgs &a, hipStream_t stream);
+
 // Each returns hipSuccess or the HIP error of the launch.
 // out = 0: the gradient is written over the logits; out = 1 / 2: float32 KL
 // rows write it rounded to bf16 / f16 into a.gout and leave the logits.
