@@ -92,6 +92,106 @@ struct RowArgs {
     void *gout;               // out != 0: [ntok][V] half-precision gradient rows
 };
 
+// Launch shape of the fused row kernels for a row of V values (16-byte
+// vectors of 4 float32 or 8 bf16 values when vec, single elements
+// otherwise): block threads x nv vectors hold the row in registers (nv = 0:
+// the online variant, which streams it); pf: the next row streams into LDS
+// meanwhile; rl: registers are refilled with the next row as the gradient
+// is stored; hk: chunks the online float32 variant holds in registers.
+struct RowShape {
+    int block, nv;
+    bool pf, rl;
+    int hk;
+};
+
+__host__ __device__ inline RowShape row_shape(bool f32, bool vec, int64_t V)
+{
+    if (!vec)
+        return {256, 0, false, false, 0};
+    const int64_t nvec = V / (f32 ? 4 : 8);
+    if (nvec <= 64)
+        return {64, 1, false, false, 0};
+    if (nvec <= 128)
+        return {64, 2, false, false, 0};
+    if (nvec <= 256)
+        return {64, 4, false, false, 0};
+    if (f32) {
+        if (nvec <= 512)
+            return {64, 8, false, false, 0};
+        if (nvec <= 1024)
+            return {256, 4, false, false, 0};
+        if (nvec <= 2048)
+            return {256, 8, false, false, 0};
+        // One block per CU, the next row streaming into LDS.  At V = 32000
+        // 1024 threads x 8 vectors run the KL and CE 1.6-2.2% faster than
+        // 512 x 16 (the same 128 KB row, twice the waves to hide the
+        // reductions' latency).
+        if (nvec <= 4096)
+            return {512, 8, true, false, 0};
+        if (nvec <= 8192)
+            return {1024, 8, true, false, 0};
+        // Rows past the registers, online: the row's first four chunks (64
+        // registers a thread) in registers, the next part in LDS, the rest
+        // streamed twice.
+        return {1024, 0, false, false, 4};
+    }
+    // bf16 widens to twice its register footprint: at most 8 vectors (64
+    // values) per thread, except with the refill, where one 1024-thread
+    // block per CU holds the whole row and refills its registers with the
+    // next row as the gradient is stored.
+    if (nvec <= 1024)
+        return {256, 4, false, false, 0};
+    if (nvec <= 4096)
+        return {512, 8, true, false, 0};
+    if (nvec <= 1024 * 19)
+        return {1024, 19, false, true, 0};
+    return {1024, 0, false, false, 0};
+}
+
+// Vectors per thread per chunk of the online variant (n values a vector).
+__host__ __device__ constexpr int online_unroll_n(int n, int hk)
+{
+    return n == 1 ? 16 : (hk > 0 ? 4 : 8);
+}
+
+// Dynamic LDS of a row kernel launch, in this order: [pf: block x nv
+// 16-byte slots][KL: two V-bit row bitmaps, 4-word aligned][online: lds_vecs
+// 16-byte slots of the current row, whole units of block vectors, after
+// the hk held chunks, as many as fit in max_dyn and the row needs].
+struct RowLds {
+    size_t bitmap_off, lrow_off, bytes;
+    int64_t lds_vecs;
+};
+
+__host__ __device__ inline RowLds row_lds(const RowShape &sh, bool kl, int64_t V, int n,
+                                          size_t raw_bytes, size_t max_dyn)
+{
+    RowLds L{};
+    size_t at = sh.pf ? (size_t)sh.block * (sh.nv > 0 ? sh.nv : 1) * 16 : 0;
+    L.bitmap_off = at;
+    if (kl)
+        at += ((2 * (size_t)((V + 31) >> 5) + 3) & ~size_t(3)) * sizeof(uint32_t);
+    L.lrow_off = at;
+    L.lds_vecs = 0;
+    if (sh.nv == 0) {
+        const size_t unit = (size_t)sh.block * raw_bytes;
+        const size_t room = at < max_dyn ? (max_dyn - at) / unit : 0;
+        const int64_t nvec = V / n;
+        const int64_t held = (int64_t)sh.hk * sh.block * online_unroll_n(n, sh.hk);
+        const int64_t rest = nvec > held ? nvec - held : 0;
+        const int64_t units = (rest + sh.block - 1) / sh.block;
+        const int64_t keep = (int64_t)room < units ? (int64_t)room : units;
+        L.lds_vecs = keep * sh.block;
+        at += (size_t)keep * unit;
+    }
+    L.bytes = at;
+    return L;
+}
+
+// Dynamic LDS a row kernel block may take: 160 KB per CU on gfx950, less a
+// margin for the kernel's static arrays (under 1 KB).
+constexpr size_t kMaxDynLds = 160 * 1024 - 1024;
+
 // One call of the split-row kernels: rows held by S co-resident
 // workgroups that swap per-part statistics through a mailbox.
 struct SplitArgs {
@@ -297,5 +397,25 @@ int blocks_per_cu(const void *fn, int block, size_t lds);
 constexpr int64_t kMaxKlVocab = int64_t(1) << 19;
 // Largest top-k k.
 constexpr int64_t kMaxTopk = 2048;
+
+// Top-k candidate buffer of one wave: the smallest power of two (512 ...
+// 4096 entries) that holds k kept entries, one sub-tile of `sub` values
+// (64 lanes x one 16-byte vector) and half of max(k, sub) spare.  Without
+// the spare a compaction leaves room for no more than one sub-tile, and the
+// buffer compacts on nearly every sub-tile that holds a candidate (float32
+// k = 256 at V = 151936 in 512 entries: 5.6 ms instead of 1.7).
+__host__ __device__ constexpr int topk_cap(int64_t k, int sub)
+{
+    const int64_t need = k + sub + (k > sub ? k : sub) / 2;
+    return need <= 512 ? 512 : need <= 1024 ? 1024 : need <= 2048 ? 2048 : 4096;
+}
+
+// Mid-row compactions may stop at a radix bin edge that keeps up to this
+// many entries: a quarter of the way from k to the next compaction's
+// trigger (cap - sub).
+__host__ __device__ constexpr int topk_sel_limit(int k, int cap, int sub)
+{
+    return k + (cap - sub - k) / 4;
+}
 
 }  // namespace vl

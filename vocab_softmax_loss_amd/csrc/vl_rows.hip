@@ -66,7 +66,7 @@ namespace vl {
 template <int N>
 constexpr int online_unroll(int hk = 0)
 {
-    return N == 1 ? 16 : (hk > 0 ? 4 : 8);
+    return online_unroll_n(N, hk);
 }
 
 // PF (staged only): stream the next row into an LDS buffer with asynchronous
@@ -698,45 +698,27 @@ __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NV, PF>())) void 
 
 namespace {
 
-// Dynamic LDS a block may take: 160 KB per CU on gfx950, less a margin for
-// the kernel's static arrays (under 1 KB).
-constexpr size_t kMaxDynLds = 160 * 1024 - 1024;
-
 template <int OUT, int DT, bool KL, int BLOCK, int NV, bool VEC, bool PF = false,
           bool RL = false, int HK = 0>
 hipError_t launch_one(const RowArgs &a, hipStream_t st)
 {
     auto fn = row_loss_kernel<DT, KL, BLOCK, NV, VEC, PF, RL, HK, OUT>;
     RowArgs args = a;
-    size_t lds = 0;
-    if (PF)
-        lds += (size_t)BLOCK * (NV > 0 ? NV : 1) * 16;
-    if (KL)
-        lds += ((2 * (size_t)((a.V + 31) >> 5) + 3) & ~size_t(3)) * sizeof(uint32_t);
-    args.lds_vecs = 0;
-    if (NV == 0) {
-        // Online: after the HK chunks held in registers, the rest of LDS
-        // keeps the row's next vectors, in units of BLOCK, for pass 2, which
-        // reads them from there instead of HBM.  Those are the first read in
-        // pass 1, the least likely to be still cached.
-        const size_t unit = (size_t)BLOCK * sizeof(typename RowIO<DT, VEC>::Raw);
-        const size_t room = lds < kMaxDynLds ? (kMaxDynLds - lds) / unit : 0;
-        const int64_t nvec = a.V / RowIO<DT, VEC>::N;
-        const int64_t held = (int64_t)HK * BLOCK * online_unroll<RowIO<DT, VEC>::N>(HK);
-        const int64_t rest = nvec > held ? nvec - held : 0;
-        const int64_t units = (rest + BLOCK - 1) / BLOCK;
-        const int64_t keep = (int64_t)room < units ? (int64_t)room : units;
-        args.lds_vecs = keep * BLOCK;
-        lds += (size_t)keep * unit;
-    }
-    {
-        if (lds > 65536) {
-            hipError_t e = hipFuncSetAttribute((const void *)fn,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)lds);
-            if (e != hipSuccess)
-                return e;
-        }
+    // Online: after the HK chunks held in registers, the rest of LDS keeps
+    // the row's next vectors, in units of BLOCK, for pass 2, which reads
+    // them from there instead of HBM.  Those are the first read in pass 1,
+    // the least likely to be still cached.
+    const RowLds L = row_lds(RowShape{BLOCK, NV, PF, RL, HK}, KL, a.V, RowIO<DT, VEC>::N,
+                             sizeof(typename RowIO<DT, VEC>::Raw), kMaxDynLds);
+    const size_t lds = L.bytes;
+    args.lds_vecs = L.lds_vecs;
+    if (lds > kMaxDynLds)
+        return hipErrorInvalidValue;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void *)fn,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
     }
     int per_cu = blocks_per_cu((const void *)fn, BLOCK, lds);
     if (NV == 0 && per_cu > 1)
@@ -749,54 +731,44 @@ hipError_t launch_one(const RowArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
-// Staged variants: BLOCK threads x NV vectors cover the row.
+// The instantiation of the shape row_shape picks (its table, in
+// vl_launch.hpp, is the one place the shapes are chosen).
 template <int DT, bool KL, int OUT>
 hipError_t launch_dt(const RowArgs &a, hipStream_t st, bool vec)
 {
-    constexpr int N = RowIO<DT, true>::N;
+    const RowShape s = row_shape(DT == kF32, vec, a.V);
+    auto is = [&](int block, int nv, bool pf, bool rl, int hk) {
+        return s.block == block && s.nv == nv && s.pf == pf && s.rl == rl && s.hk == hk;
+    };
     if (!vec)
-        return launch_one<OUT, DT, KL, 256, 0, false>(a, st);
-    const int64_t nvec = a.V / N;
-    if (nvec <= 64)
+        return is(256, 0, false, false, 0) ? launch_one<OUT, DT, KL, 256, 0, false>(a, st)
+                                           : hipErrorInvalidValue;
+    if (is(64, 1, false, false, 0))
         return launch_one<OUT, DT, KL, 64, 1, true>(a, st);
-    if (nvec <= 128)
+    if (is(64, 2, false, false, 0))
         return launch_one<OUT, DT, KL, 64, 2, true>(a, st);
-    if (nvec <= 256)
+    if (is(64, 4, false, false, 0))
         return launch_one<OUT, DT, KL, 64, 4, true>(a, st);
+    if (is(256, 4, false, false, 0))
+        return launch_one<OUT, DT, KL, 256, 4, true>(a, st);
+    if (is(512, 8, true, false, 0))
+        return launch_one<OUT, DT, KL, 512, 8, true, true>(a, st);
     if constexpr (DT == kF32) {
-        if (nvec <= 512)
+        if (is(64, 8, false, false, 0))
             return launch_one<OUT, DT, KL, 64, 8, true>(a, st);
-        if (nvec <= 1024)
-            return launch_one<OUT, DT, KL, 256, 4, true>(a, st);
-        if (nvec <= 2048)
+        if (is(256, 8, false, false, 0))
             return launch_one<OUT, DT, KL, 256, 8, true>(a, st);
-        // One block per CU, the next row streaming into LDS.  At V = 32000
-        // 1024 threads x 8 vectors run the KL and CE 1.6-2.2% faster than
-        // 512 x 16 (the same 128 KB row, twice the waves to hide the
-        // reductions' latency).
-        if (nvec <= 4096)
-            return launch_one<OUT, DT, KL, 512, 8, true, true>(a, st);
-        if (nvec <= 8192)
+        if (is(1024, 8, true, false, 0))
             return launch_one<OUT, DT, KL, 1024, 8, true, true>(a, st);
+        if (is(1024, 0, false, false, 4))
+            return launch_one<OUT, DT, KL, 1024, 0, true, false, false, 4>(a, st);
     } else {
-        // bf16 widens to twice its register footprint: at most 8 vectors
-        // (64 values) per thread.
-        if (nvec <= 1024)
-            return launch_one<OUT, DT, KL, 256, 4, true>(a, st);
-        if (nvec <= 4096)
-            return launch_one<OUT, DT, KL, 512, 8, true, true>(a, st);
-        // One 1024-thread block per CU holds the whole row in registers and
-        // refills them with the next row as the gradient is stored.
-        if (nvec <= 1024 * 19)
+        if (is(1024, 19, false, true, 0))
             return launch_one<OUT, DT, KL, 1024, 19, true, false, true>(a, st);
+        if (is(1024, 0, false, false, 0))
+            return launch_one<OUT, DT, KL, 1024, 0, true>(a, st);
     }
-    // Rows past the registers, online: float32 holds the row's first four
-    // chunks (64 registers a thread) in registers, the next part in LDS, and
-    // streams the rest twice.
-    if constexpr (DT == kF32)
-        return launch_one<OUT, DT, KL, 1024, 0, true, false, false, 4>(a, st);
-    else
-        return launch_one<OUT, DT, KL, 1024, 0, true>(a, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

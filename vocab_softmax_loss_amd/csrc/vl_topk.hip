@@ -396,9 +396,7 @@ __global__ __launch_bounds__(WPB * kWave, (CAP <= 1024 ? 4 : 1)) void topk_kerne
     uint32_t *ids = s_id[w];
     uint32_t *hist = s_hist[w];
     const int k = (int)a.k;
-    // Mid-row compactions may stop at a bound that keeps up to this many
-    // entries: a quarter of the way from k to the next compaction's trigger.
-    const int kSelLimit = k + (CAP - SUB - k) / 4;
+    const int kSelLimit = topk_sel_limit(k, CAP, SUB);
     const uint32_t nvec = (uint32_t)(a.V / N);
     const char *rowp =
         reinterpret_cast<const char *>(a.logits) + row * a.V * (int64_t)elt_bytes<DT>();
@@ -592,18 +590,12 @@ hipError_t launch_cap(const TopkArgs &a, hipStream_t st)
 template <int DT, bool VEC>
 hipError_t launch_dt(const TopkArgs &a, hipStream_t st)
 {
-    // The buffer holds k kept entries and one sub-tile, and after each
-    // compaction it needs room for a few more sub-tiles' candidates, or it
-    // compacts on every sub-tile that holds one: at least half of max(k,
-    // sub-tile) spare.  (float32 k = 256 at V = 151936 in 512 entries, with
-    // no spare: 5.6 ms; in 1024: see the design notes.)
-    constexpr int SUB = kWave * RowIO<DT, VEC>::N;
-    const int64_t need = a.k + SUB + (a.k > SUB ? a.k : SUB) / 2;
-    if (need <= 512)
+    const int cap = topk_cap(a.k, kWave * RowIO<DT, VEC>::N);
+    if (cap == 512)
         return launch_cap<DT, VEC, 512>(a, st);
-    if (need <= 1024)
+    if (cap == 1024)
         return launch_cap<DT, VEC, 1024>(a, st);
-    if (need <= 2048)
+    if (cap == 2048)
         return launch_cap<DT, VEC, 2048>(a, st);
     return launch_cap<DT, VEC, 4096>(a, st);
 }
