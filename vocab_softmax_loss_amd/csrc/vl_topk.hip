@@ -40,6 +40,8 @@
 // values.
 #include <math.h>
 
+#include <type_traits>
+
 #include "vl_device.hpp"
 #include "vl_launch.hpp"
 
@@ -215,103 +217,132 @@ __device__ __forceinline__ uint64_t sort_pair(uint32_t key, uint32_t id)
     return ((uint64_t)key << 32) | (uint32_t)~id;
 }
 
-__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int j)
+// The value of lane (this lane ^ J): DPP within quads for J = 1, 2,
+// ds_bpermute otherwise.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t v, int lane)
 {
-    const int addr = (lane_id() ^ j) << 2;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
+    if constexpr (J == 1)
+        return dpp_u32<0xB1>(v, v);  // quad_perm [1, 0, 3, 2]
+    else if constexpr (J == 2)
+        return dpp_u32<0x4E>(v, v);  // quad_perm [2, 3, 0, 1]
+    else
+        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ J) << 2, (int)v);
 }
 
-// One compare-exchange step of a bitonic sort whose partner distance
-// 64 JE is a multiple of the wave: entry i = 64 e + lane pairs with the
-// entry JE registers away in the same lane.  Blocks of kk entries whose
-// index has bit kk clear end descending, the others ascending.
-template <int JE, int EB>
-__device__ __forceinline__ void bitonic_step_regs(uint64_t (&K)[EB], int EP, int kk)
+template <int J>
+__device__ __forceinline__ uint64_t xor_lanes(uint64_t v, int lane)
 {
-#pragma unroll
-    for (int e = 0; e < EB; ++e) {
-        if ((e & JE) || (e | JE) >= EB)
-            continue;
-        if (e >= EP)
-            break;
-        const bool desc = ((e * kWave) & kk) == 0;
-        const uint64_t a = K[e], b = K[e | JE];
-        const bool sw = desc ? a < b : a > b;
-        K[e] = sw ? b : a;
-        K[e | JE] = sw ? a : b;
-    }
+    return ((uint64_t)xor_lanes<J>((uint32_t)(v >> 32), lane) << 32) |
+           xor_lanes<J>((uint32_t)v, lane);
 }
 
-// Sort K over P = 64 EP entries (P a power of two) descending; entry i is
-// register i / 64 of lane i % 64.
-template <int EB>
-__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&K)[EB], int EP)
+// One compare-exchange step of a descending bitonic sort over 64 EP entries
+// (entry i is register i / 64 of lane i % 64): partner i ^ J; blocks of KK
+// entries whose index has bit KK clear end descending, the others
+// ascending.  Partners in other lanes are exchanged for all registers
+// first, then compared, so one wait covers a step.
+template <int KK, int J, int EP, typename T>
+__device__ __forceinline__ void bitonic_step(T (&K)[EP], int lane)
 {
-    const int lane = lane_id();
-    const int P = kWave * EP;
-    for (int kk = 2; kk <= P; kk <<= 1) {
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-            if (j < kWave) {
-                const bool lower = (lane & j) == 0;
+    if constexpr (J < kWave) {
+        T b[EP];
 #pragma unroll
-                for (int e = 0; e < EB; ++e) {
-                    if (e >= EP)
-                        break;
-                    const int i = e * kWave + lane;
-                    const bool desc = (i & kk) == 0;
-                    const uint64_t b = lane_xor_u64(K[e], j);
-                    const uint64_t a = K[e];
-                    const bool take_max = lower == desc;
-                    K[e] = take_max ? (a > b ? a : b) : (a < b ? a : b);
-                }
-            } else {
-                switch (j / kWave) {
-                case 1: bitonic_step_regs<1>(K, EP, kk); break;
-                case 2: bitonic_step_regs<2>(K, EP, kk); break;
-                case 4: bitonic_step_regs<4>(K, EP, kk); break;
-                case 8: bitonic_step_regs<8>(K, EP, kk); break;
-                case 16: bitonic_step_regs<16>(K, EP, kk); break;
-                default: bitonic_step_regs<32>(K, EP, kk); break;
-                }
-            }
+        for (int e = 0; e < EP; ++e)
+            b[e] = xor_lanes<J>(K[e], lane);
+        const bool lower = (lane & J) == 0;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            const bool desc = ((e * kWave + lane) & KK) == 0;
+            const T a = K[e];
+            K[e] = (lower == desc) ? (a > b[e] ? a : b[e]) : (a < b[e] ? a : b[e]);
+        }
+    } else {
+        constexpr int JE = J / kWave;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            if (e & JE)
+                continue;
+            const bool desc = ((e * kWave) & KK) == 0;
+            const T a = K[e], b = K[e | JE];
+            const bool sw = desc ? a < b : a > b;
+            K[e] = sw ? b : a;
+            K[e | JE] = sw ? a : b;
         }
     }
 }
 
-// The k winners in keys/ids[0..k) (any order): sort them and write the ids
-// and renormalised probabilities in rank order.  EB registers per lane hold
-// up to 64 EB entries.
-template <int EB>
-__device__ __forceinline__ void write_ranked(const uint32_t *keys, const uint32_t *ids, int k, uint32_t *out_ids,
-                                             float *out_p)
+template <int KK, int J, int EP, typename T>
+__device__ __forceinline__ void bitonic_merge(T (&K)[EP], int lane)
+{
+    bitonic_step<KK, J, EP>(K, lane);
+    if constexpr (J > 1)
+        bitonic_merge<KK, J / 2, EP>(K, lane);
+}
+
+// Sort the 64 EP entries descending: stages KK = 2, 4, ..., 64 EP, fully
+// unrolled.  `lane` is the lane index.
+template <int KK, int EP, typename T>
+__device__ __forceinline__ void bitonic_sort_desc(T (&K)[EP], int lane)
+{
+    bitonic_merge<KK, KK / 2, EP>(K, lane);
+    if constexpr (KK < kWave * EP)
+        bitonic_sort_desc<KK * 2, EP>(K, lane);
+}
+
+// The k winners in keys/ids[0..k), in id order: sort them and write the ids
+// and renormalised probabilities in rank order; 64 EP >= k entries in EP
+// registers a lane.  bf16 keys (BF) carry the value in their upper 16 bits,
+// so a 32-bit entry holds the key's upper half above 0xFFFF - (buffer
+// index): descending is value descending, index (= id) ascending.
+// float32 entries are 64-bit: the key above the complemented id.
+template <int EP, bool BF>
+__device__ __forceinline__ void write_ranked(const uint32_t *keys, const uint32_t *ids, int k,
+                                             uint32_t *out_ids, float *out_p)
 {
     const int lane = lane_id();
-    int EP = 1;  // registers in use: 64 EP is the power of two >= k
-    while (kWave * EP < k)
-        EP <<= 1;
-    uint64_t K[EB];
+    typedef typename std::conditional<BF, uint32_t, uint64_t>::type T;
+    T K[EP];
 #pragma unroll
-    for (int e = 0; e < EB; ++e) {
+    for (int e = 0; e < EP; ++e) {
         const int i = lane + kWave * e;
-        K[e] = i < k ? sort_pair(keys[i], ids[i]) : 0ull;
+        if constexpr (BF)
+            K[e] = i < k ? ((keys[i] & 0xFFFF0000u) | (0xFFFFu - (uint32_t)i)) : 0u;
+        else
+            K[e] = i < k ? sort_pair(keys[i], ids[i]) : 0ull;
     }
-    bitonic_sort_desc<EB>(K, EP);
-
-    const float v0 = key_value((uint32_t)(__builtin_amdgcn_readlane((int)(uint32_t)(K[0] >> 32), 0)));
+    bitonic_sort_desc<2, EP>(K, lane);
+    // the entry's key (bf16: the lower half is 0 for values >= +0 and
+    // 0xFFFF below, as order_key makes it)
+    auto key_of = [](T x) {
+        if constexpr (BF) {
+            const uint32_t hi = x & 0xFFFF0000u;
+            return hi | ((hi & 0x80000000u) ? 0u : 0xFFFFu);
+        } else {
+            return (uint32_t)(x >> 32);
+        }
+    };
+    const float v0 = key_value((uint32_t)__builtin_amdgcn_readlane((int)key_of(K[0]), 0));
+    float ev[EP];
     float z = 0.f;
 #pragma unroll
-    for (int e = 0; e < EB; ++e)
+    for (int e = 0; e < EP; ++e) {
+        ev[e] = __expf(key_value(key_of(K[e])) - v0);
         if (lane + kWave * e < k)
-            z += __expf(key_value((uint32_t)(K[e] >> 32)) - v0);
+            z += ev[e];
+    }
     const float Z = wave_sum(z);
 #pragma unroll
-    for (int e = 0; e < EB; ++e) {
+    for (int e = 0; e < EP; ++e) {
         const int i = lane + kWave * e;
+        // Non-temporal: nothing reads the output soon (16384 x 151936
+        // bf16, k = 256: 16 us less than ordinary stores).
         if (i < k) {
-            out_ids[i] = ~(uint32_t)K[e];
-            out_p[i] = __expf(key_value((uint32_t)(K[e] >> 32)) - v0) / Z;
+            if constexpr (BF)
+                __builtin_nontemporal_store(ids[0xFFFFu - (K[e] & 0xFFFFu)], out_ids + i);
+            else
+                __builtin_nontemporal_store(~(uint32_t)K[e], out_ids + i);
+            __builtin_nontemporal_store(ev[e] / Z, out_p + i);
         }
     }
 }
@@ -362,8 +393,8 @@ __device__ __forceinline__ void write_ranked_lds(uint32_t *keys, uint32_t *ids, 
         z += __expf(key_value(keys[i]) - v0);
     const float Z = wave_sum(z);
     for (int i = lane; i < k; i += kWave) {
-        out_ids[i] = ids[i];
-        out_p[i] = __expf(key_value(keys[i]) - v0) / Z;
+        __builtin_nontemporal_store(ids[i], out_ids + i);
+        __builtin_nontemporal_store(__expf(key_value(keys[i]) - v0) / Z, out_p + i);
     }
 }
 
@@ -381,6 +412,11 @@ __global__ __launch_bounds__(WPB * kWave, (CAP <= 1024 ? 4 : 1)) void topk_kerne
     // k <= min(CAP - SUB, kMaxTopk); the sort pads k to a power of two.
     constexpr int kMaxK = (CAP - SUB) < kMaxTopk ? (CAP - SUB) : (int)kMaxTopk;
     constexpr int kSortRegs = pow2_ceil(kMaxK) / kWave > 0 ? pow2_ceil(kMaxK) / kWave : 1;
+    // Registers a lane may take for the final sort (64 per register a
+    // lane): up to 8 in the four-waves-per-SIMD variants (CAP <= 1024); the
+    // larger buffers serve k above 256 (bf16) or 512 (float32) and sort in
+    // LDS.
+    constexpr int kRegSort = CAP <= 1024 ? (kSortRegs < 8 ? kSortRegs : 8) : 0;
 
     __shared__ uint32_t s_key[WPB][CAP];
     __shared__ uint32_t s_id[WPB][CAP];
@@ -569,10 +605,26 @@ __global__ __launch_bounds__(WPB * kWave, (CAP <= 1024 ? 4 : 1)) void topk_kerne
     // exactly k winners, in id order, then written at their ranks
     wave_lds_sync();
     select_compact<E>(keys, ids, cnt, k, hist);  // leaves exactly k entries
-    if constexpr (kSortRegs <= 8)
-        write_ranked<kSortRegs>(keys, ids, k, a.ids + row * a.k, a.probs + row * a.k);
-    else
-        write_ranked_lds(keys, ids, k, a.ids + row * a.k, a.probs + row * a.k);
+    uint32_t *oi = a.ids + row * a.k;
+    float *op = a.probs + row * a.k;
+    constexpr bool BF = DT == kBF16;
+    if (k <= kWave && kRegSort >= 1) {
+        write_ranked<1, BF>(keys, ids, k, oi, op);
+    } else if (k <= 2 * kWave && kRegSort >= 2) {
+        write_ranked<2, BF>(keys, ids, k, oi, op);
+    } else if (k <= 4 * kWave) {
+        if constexpr (kRegSort >= 4)
+            write_ranked<4, BF>(keys, ids, k, oi, op);
+        else
+            write_ranked_lds(keys, ids, k, oi, op);
+    } else if (k <= 8 * kWave) {
+        if constexpr (kRegSort >= 8)
+            write_ranked<8, BF>(keys, ids, k, oi, op);
+        else
+            write_ranked_lds(keys, ids, k, oi, op);
+    } else {
+        write_ranked_lds(keys, ids, k, oi, op);
+    }
 }
 
 namespace {
