@@ -602,9 +602,18 @@ __global__ __launch_bounds__(WPB * kWave, (CAP <= 1024 ? 4 : 1)) void topk_kerne
         t0 += TILE;
     }
 
-    // exactly k winners, in id order, then written at their ranks
+    // exactly k winners, in id order, then written at their ranks; the
+    // selection runs over as many registers as the buffer's fill needs
+    // (it usually holds far fewer than CAP entries by the row's end)
     wave_lds_sync();
-    select_compact<E>(keys, ids, cnt, k, hist);  // leaves exactly k entries
+    if (E > 2 && cnt <= 2 * kWave)
+        select_compact<(E > 2 ? 2 : E)>(keys, ids, cnt, k, hist);
+    else if (E > 4 && cnt <= 4 * kWave)
+        select_compact<(E > 4 ? 4 : E)>(keys, ids, cnt, k, hist);
+    else if (E > 8 && cnt <= 8 * kWave)
+        select_compact<(E > 8 ? 8 : E)>(keys, ids, cnt, k, hist);
+    else
+        select_compact<E>(keys, ids, cnt, k, hist);  // leaves exactly k entries
     uint32_t *oi = a.ids + row * a.k;
     float *op = a.probs + row * a.k;
     constexpr bool BF = DT == kBF16;
