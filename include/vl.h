@@ -293,9 +293,13 @@ int vl_kl_slice_bwd(void *logits, int dtype, int64_t ld, int64_t off, int64_t wi
                     int64_t ntok, const vl_range *rng, float coef, hipStream_t stream);
 
 /*
- * Scratch bytes vl_head_kl needs for `chunk` rows at a time: float32 logits
- * [chunk][V], the half-precision hidden rows [chunk][hs] and gradient
- * [chunk][V], and a 64 MiB GEMM workspace, each 256-byte aligned.
+ * Scratch bytes vl_head_kl needs for `chunk` rows at a time, each region
+ * 256-byte aligned: float32 logits [chunk][V], the half-precision hidden
+ * rows [chunk][hs rounded up to 64], the half-precision gradient [chunk][V],
+ * the (max, sum exp) records of every 128 columns [chunk][2 ceil(V/256)]
+ * (8 bytes each), lse [chunk], the loss sums of every 2048 columns
+ * [chunk][ceil(V/2048)] (float32), and a 64 MiB GEMM workspace.  0 for
+ * invalid sizes.
  */
 size_t vl_head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
 
@@ -318,12 +322,15 @@ size_t vl_head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
  *   scratch device buffer of at least vl_head_scratch_bytes(min(chunk,
  *           ntok), V, hs) bytes, owned by the caller; its contents on entry
  *           do not matter and are undefined after the call.
- * The two products run in hipBLASLt; its handle is created on the first
- * call on each device and kept until the process ends (the only allocation
- * the library makes).  The first call with a given shape on a device also
- * times up to 16 hipBLASLt algorithms for each product on `stream` (the
- * three fastest a second time) and keeps the fastest for later calls; that
- * one call waits for the stream.  Under
+ * The logits product runs on this library's matrix-core kernel, which also
+ * forms each row's softmax statistics, when hs is a multiple of 8 and x and
+ * w are 16-byte aligned (otherwise in hipBLASLt, followed by the fused KL
+ * row kernel); the dx product runs in hipBLASLt.  The hipBLASLt handle is
+ * created on the first call on each device and kept until the process ends
+ * (the only allocation the library makes).  The first call with a given
+ * shape on a device also times up to 16 hipBLASLt algorithms for each
+ * hipBLASLt product on `stream` (the three fastest a second time) and keeps
+ * the fastest for later calls; that one call waits for the stream.  Under
  * stream capture nothing is timed and hipBLASLt's first choice runs.
  * Limits: 1 <= k <= V <= 2^19, hs >= 1, chunk >= 1.
  * Returns VL_ELAUNCH if hipBLASLt finds no algorithm or rejects a call.
@@ -334,9 +341,10 @@ int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
                size_t scratch_bytes, hipStream_t stream);
 
 /*
- * Scratch bytes vl_head_topk needs for `chunk` rows at a time: float32
- * logits [chunk][V], the half-precision hidden rows [chunk][hs] and a
- * 64 MiB GEMM workspace, each 256-byte aligned (0 for invalid sizes).
+ * Scratch bytes vl_head_topk needs for `chunk` rows at a time, each region
+ * 256-byte aligned: float32 logits [chunk][V], the half-precision hidden
+ * rows [chunk][hs rounded up to 64] and a 64 MiB GEMM workspace (0 for
+ * invalid sizes).
  */
 size_t vl_head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
 
@@ -356,8 +364,10 @@ size_t vl_head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
  *   scratch device buffer of at least vl_head_topk_scratch_bytes(min(chunk,
  *           ntok), V, hs) bytes, owned by the caller; contents on entry do
  *           not matter and are undefined after the call.
- * The product runs in hipBLASLt, as in vl_head_kl (same handle, same
- * one-time timing of its algorithms per shape, which waits for `stream`).
+ * The product runs on this library's matrix-core kernel when hs is a
+ * multiple of 8 and x and w are 16-byte aligned, otherwise in hipBLASLt, as
+ * in vl_head_kl (same handle, same one-time timing of its algorithms per
+ * shape, which waits for `stream`).
  * Limits: 1 <= k <= min(V, 2048), V <= 2^31 - 1, hs >= 1, chunk >= 1,
  * ntok <= 2^31 - 1.
  */

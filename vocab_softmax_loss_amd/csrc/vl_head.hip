@@ -290,9 +290,9 @@ size_t align_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 
 // Scratch of one chunk of rows, each region 256-byte aligned:
 //   logits [chunk][V] float32, act [chunk][lda] half (lda = hs rounded up to
-//   64), dl [chunk][V] half (student side only), rec [chunk][2 ceil(V/256)]
-//   (max, sum) pairs, lse [chunk], part [chunk][ceil(V/2048)] loss sums
-//   (student side only), then the hipBLASLt workspace.
+//   64), then on the student side only dl [chunk][V] half, rec
+//   [chunk][2 ceil(V/256)] (max, sum) pairs, lse [chunk] and part
+//   [chunk][ceil(V/2048)] loss sums; then the hipBLASLt workspace.
 struct HeadLayout {
     size_t logits, act, dl, rec, lse, part, ws, total;
 };
@@ -316,8 +316,8 @@ HeadLayout head_layout(int64_t chunk, int64_t V, int64_t hs, bool student)
     L.logits = take((size_t)chunk * (size_t)V * 4);
     L.act = take((size_t)chunk * (size_t)head_lda(hs) * 2);
     L.dl = student ? take((size_t)chunk * (size_t)V * 2) : at;
-    L.rec = take((size_t)chunk * (size_t)head_nrec(V) * 8);
-    L.lse = take((size_t)chunk * 4);
+    L.rec = student ? take((size_t)chunk * (size_t)head_nrec(V) * 8) : at;
+    L.lse = student ? take((size_t)chunk * 4) : at;
     L.part = student ? take((size_t)chunk * (size_t)head_cpr_max(V) * 4) : at;
     L.ws = at;
     L.total = at + kHeadWorkspace;
