@@ -142,6 +142,29 @@ def test_head_bad_id_and_padded_teacher(vl):
 
 # ------------------------------------------------ the teacher side (vl_head_topk)
 
+@pytest.mark.parametrize("hs", [64, 20])
+def test_head_nan_weight_and_row(vl, hs):
+    """A NaN head weight row makes every row's logits hold a NaN, and a NaN
+    hidden row makes that row's logits all NaN: those rows' loss and dx are
+    NaN, as the definition gives, and the other rows still match the oracle.
+    hs = 64 runs the matrix-core product with its statistics records, 20 the
+    library product and the row kernels."""
+    ntok, V, k, chunk = 7, 999, 5, 4
+    c = gi.head_inputs(ntok, V, hs, k, 8300 + hs, DEV, torch.float16)
+    total, gscale = ntok, 64.0
+    w = c["w"].clone()
+    w[3] = float("nan")
+    loss, dx = run_head(vl, c["x"], w, c["ids"], c["probs"], total, gscale, chunk)
+    assert np.isnan(loss).all() and np.isnan(dx).all()
+    x = c["x"].clone()
+    x[2] = float("nan")
+    loss, dx = run_head(vl, x, c["w"], c["ids"], c["probs"], total, gscale, chunk)
+    assert np.isnan(loss[2]) and np.isnan(dx[2]).all()
+    keep = np.array([r for r in range(ntok) if r != 2])
+    rl, rdx = oracle_for(c["x"], c["w"], c["ids"], c["probs"], total, gscale, "f16")
+    check(loss[keep], dx[keep], rl[keep], rdx[keep], "f16")
+
+
 def run_head_topk(vl, x, w, k, chunk):
     ntok, hs = x.shape
     V = w.shape[0]

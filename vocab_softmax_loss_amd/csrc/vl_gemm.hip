@@ -273,10 +273,10 @@ __global__ __launch_bounds__(256, 1) void logits_kernel(LogitsArgs g)
                     const float oa = __shfl_xor(ra[0], 1), oz = __shfl_xor(rz[0], 1);
                     merge_rec(ra[0], rz[0], oa, oz);
                 }
-                // lane L (= l % 32) holds accumulator slot r = (L / 2)
-                // reversed in bits 4..1 of L: bit d of L chose the upper
-                // half at distance d, i.e. r bit 3 <- L bit 4, ... r bit 0
-                // <- L bit 1.
+                // lane L (= l % 32) holds accumulator slot r = L / 2: the
+                // step at distance d kept the upper half in the lanes with
+                // bit d of L set, so r's bit 3 is L's bit 4, ..., r's bit 0
+                // is L's bit 1.
                 const uint32_t L = lane & 31u;
                 const uint32_t r = L >> 1;
                 const int64_t row = rowb + i * 32 + 8 * (r / 4) + (r % 4);

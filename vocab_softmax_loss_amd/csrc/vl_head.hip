@@ -97,7 +97,9 @@ __device__ __forceinline__ float head_scalar_f32(const float *p, int64_t i)
 
 // The row's log-sum-exp from the product's (max, sum exp) records, one wave
 // per row: lse = M + ln sum_t z_t exp(a_t - M), M the largest anchor; empty
-// records (z = 0, anchor -inf) are left out.
+// records (z = 0, anchor -inf) are left out.  A NaN logit leaves its
+// record's sum NaN (the anchor skips it), and that record is kept, so the
+// row's lse, loss and gradient come out NaN as the definition gives.
 __global__ __launch_bounds__(256) void head_lse_kernel(const float2 *rec, int64_t nrec,
                                                        int64_t rows, float *lse)
 {
@@ -109,13 +111,13 @@ __global__ __launch_bounds__(256) void head_lse_kernel(const float2 *rec, int64_
     float m = -INFINITY;
     for (int64_t q = lane; q < nrec; q += kWave) {
         const float2 t = rr[q];
-        m = t.y > 0.f ? fmaxf(m, t.x) : m;
+        m = !(t.y <= 0.f) ? fmaxf(m, t.x) : m;
     }
     const float M = wave_max(m);
     float z = 0.f;
     for (int64_t q = lane; q < nrec; q += kWave) {
         const float2 t = rr[q];
-        z += t.y > 0.f ? t.y * __expf(t.x - M) : 0.f;
+        z += !(t.y <= 0.f) ? t.y * __expf(t.x - M) : 0.f;
     }
     const float Z = wave_sum(z);
     if (lane == 0)
