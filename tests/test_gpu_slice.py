@@ -189,6 +189,25 @@ def test_slices_special_rows(vl):
     assert_sliced(vl, x, ids, probs, cuts_of(V, (1000, 1000, 1000)), None, 0.5)
 
 
+def test_slices_nan_logit(vl):
+    """A NaN logit in one slice of a row makes that row's lse and loss NaN
+    (its slice's sum is NaN and the merge keeps it); the other rows come
+    out exactly as without it."""
+    V, k, n = 3000, 6, 4
+    x = gi.normal_logits(n, V, 2.0, 3750, DEV)
+    ids = gi.distinct_ids(n, V, k, 3751, DEV)
+    probs = gi.softmax_probs(n, k, 1.5, 3752, DEV)
+    cuts = cuts_of(V, (1000, 1000, 1000))
+    _, l0, s0, g0 = run_sliced(vl, x, ids, probs, cuts, None, 0.5, "window")
+    y = x.clone()
+    y[1, 2345] = float("nan")
+    _, l1, s1, g1 = run_sliced(vl, y, ids, probs, cuts, None, 0.5, "window")
+    assert np.isnan(l1[1]) and np.isnan(s1[1])
+    keep = [0, 2, 3]
+    assert np.array_equal(l1[keep], l0[keep]) and np.array_equal(s1[keep], s0[keep])
+    assert np.array_equal(g1[keep], g0[keep])
+
+
 def test_slices_unit_target_is_the_cross_entropy(vl):
     """k = 1, probs = 1: the merged loss and the slice gradients are the
     fused cross-entropy's."""

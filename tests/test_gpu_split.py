@@ -161,6 +161,25 @@ def test_split_fewer_rows_than_groups(vl, ws, dtype, V, ntok):
     check_all("ce", to_host_bytes(x), g, loss, lse, lab.cpu().numpy(), None, None, 0.5, dtype)
 
 
+@pytest.mark.parametrize("dtype,V", [("f32", 128256), ("bf16", 200000)])
+def test_split_nan_logit(vl, ws, dtype, V):
+    """A NaN logit in one part of a split row makes that row's lse and loss
+    NaN (the part's sum is NaN and the exchange keeps it); the other rows
+    come out exactly as without it."""
+    ntok, k = 9, 16
+    x = gi.normal_logits(ntok, V, 2.0, 5650, DEV, TDT[dtype])
+    ids = gi.distinct_ids(ntok, V, k, 5651, DEV)
+    probs = gi.softmax_probs(ntok, k, 1.5, 5652, DEV)
+    l0, s0, g0 = run_kl_ws(vl, x, ids, probs, None, 0.25, ws)
+    y = x.clone()
+    y[4, V - 7] = float("nan")
+    l1, s1, g1 = run_kl_ws(vl, y, ids, probs, None, 0.25, ws)
+    assert np.isnan(l1[4]) and np.isnan(s1[4])
+    keep = [r for r in range(ntok) if r != 4]
+    assert np.array_equal(l1[keep], l0[keep]) and np.array_equal(s1[keep], s0[keep])
+    assert torch.equal(g1[keep], g0[keep])
+
+
 def test_split_all_rows_outside_the_range(vl, ws):
     V = 128256
     x = gi.normal_logits(40, V, 2.0, 5600, DEV)

@@ -232,16 +232,18 @@ __global__ __launch_bounds__(256) void slice_merge_kernel(const float *parts, in
         return;
     }
     const f32x4 *pp = reinterpret_cast<const f32x4 *>(parts);
+    // Slices with no finite value (sum 0) are left out; a NaN sum (a NaN
+    // logit) is kept, so the row's lse and loss come out NaN.
     float M = -INFINITY;
     for (int64_t i = 0; i < nslice; ++i) {
         const f32x4 r = pp[i * ntok + row];
-        if (r[1] > 0.f)
+        if (!(r[1] <= 0.f))
             M = fmaxf(M, r[0]);
     }
     float S = 0.f;
     for (int64_t i = 0; i < nslice; ++i) {
         const f32x4 r = pp[i * ntok + row];
-        if (r[1] > 0.f)
+        if (!(r[1] <= 0.f))
             S += r[1] * __expf(r[0] - M);
     }
     const float L = M + __logf(S);

@@ -313,7 +313,8 @@ struct SplitKernel {
         }
         const bool bad = ballot(!ok) != 0;
         broken = broken || bad;
-        const bool live = lane < S && rz > 0.f;
+        // parts with no finite value (sum 0) are left out; a NaN sum is kept
+        const bool live = lane < S && !(rz <= 0.f);
         const float M = wave_max(live ? ra : -INFINITY);
         const float Z = wave_sum(live ? rz * __expf(ra - M) : 0.f);
         float lse = M + __logf(Z);
