@@ -283,6 +283,10 @@ def other_workload(name, dev):
         loss = torch.empty(ntok, device=dev)
         scratch = torch.empty(vl.vl_head_scratch_bytes(chunk, V, hs), dtype=torch.uint8,
                               device=dev)
+        # set-up, before the warm-up: pick the dx product's hipBLASLt
+        # algorithm for this shape (the call waits while it times them)
+        vl.vl_head_kl(c["x"], c["w"], c["ids"], c["probs"], dx, loss, ntok, gscale, chunk,
+                      scratch, tune=True)
         calls = [("head", lambda: vl.vl_head_kl(c["x"], c["w"], c["ids"], c["probs"], dx, loss,
                                                 ntok, gscale, chunk, scratch))]
         nbytes = {"head": None}
@@ -298,6 +302,7 @@ def other_workload(name, dev):
         probs = torch.empty((ntok, k), device=dev)
         scratch = torch.empty(vl.vl_head_topk_scratch_bytes(chunk, V, hs), dtype=torch.uint8,
                               device=dev)
+        vl.vl_head_topk(c["x"], c["w"], k, ids, probs, chunk, scratch, tune=True)
         calls = [("head_topk", lambda: vl.vl_head_topk(c["x"], c["w"], k, ids, probs, chunk,
                                                        scratch))]
         nbytes = {"head_topk": None}

@@ -19,7 +19,7 @@
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller.  The library keeps
  *     no reference after the call returns and allocates no memory (except
- *     vl_head_kl's hipBLASLt handle, below).
+ *     the head calls' hipBLASLt handle, below).
  *   - Calls are asynchronous on `stream` (0 = the null stream of the current
  *     device); the caller observes completion on that stream.
  *   - Matrices are row-major and contiguous: row r of logits starts at
@@ -327,11 +327,10 @@ size_t vl_head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
  * w are 16-byte aligned (otherwise in hipBLASLt, followed by the fused KL
  * row kernel); the dx product runs in hipBLASLt.  The hipBLASLt handle is
  * created on the first call on each device and kept until the process ends
- * (the only allocation the library makes).  The first call with a given
- * shape on a device also times up to 16 hipBLASLt algorithms for each
- * hipBLASLt product on `stream` (the three fastest a second time) and keeps
- * the fastest for later calls; that one call waits for the stream.  Under
- * stream capture nothing is timed and hipBLASLt's first choice runs.
+ * (the only allocation the library makes).  Each hipBLASLt product runs the
+ * algorithm that vl_head_kl_tune (or vl_head_topk_tune) chose for its shape
+ * on this device, or, for a shape not tuned, hipBLASLt's first choice; the
+ * call never waits for the stream.
  * Limits: 1 <= k <= V <= 2^19, hs >= 1, chunk >= 1.
  * Returns VL_ELAUNCH if hipBLASLt finds no algorithm or rejects a call.
  */
@@ -339,6 +338,23 @@ int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
                const float *probs, int64_t k, float *dx, float *loss, int64_t ntok, int64_t V,
                int64_t hs, int64_t total, float gscale, int64_t chunk, void *scratch,
                size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * vl_head_kl_tune -- vl_head_kl (same arguments, same results) that first
+ * picks the algorithm of each hipBLASLt product shape not yet tuned on this
+ * device, for callers who set up once and then call vl_head_kl: it times
+ * up to 16 of hipBLASLt's candidates on `stream` (one untimed and two timed
+ * runs each, the three fastest again, four runs each in turns) on the
+ * call's own operands, and keeps the fastest for every later head call with
+ * that shape.  This call waits for `stream` while it times (the host
+ * blocks); shapes already tuned run as in vl_head_kl.  Under stream capture
+ * nothing is timed.  Tuned and untuned calls may differ in float32 rounding
+ * of the products (another algorithm sums in another order).
+ */
+int vl_head_kl_tune(const float *x, const void *w, int wdtype, const uint32_t *ids,
+                    const float *probs, int64_t k, float *dx, float *loss, int64_t ntok,
+                    int64_t V, int64_t hs, int64_t total, float gscale, int64_t chunk,
+                    void *scratch, size_t scratch_bytes, hipStream_t stream);
 
 /*
  * Scratch bytes vl_head_topk needs for `chunk` rows at a time, each region
@@ -366,14 +382,24 @@ size_t vl_head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
  *           not matter and are undefined after the call.
  * The product runs on this library's matrix-core kernel when hs is a
  * multiple of 8 and x and w are 16-byte aligned, otherwise in hipBLASLt, as
- * in vl_head_kl (same handle, same one-time timing of its algorithms per
- * shape, which waits for `stream`).
+ * in vl_head_kl (same handle, same per-shape algorithm choice; the call
+ * never waits for the stream).
  * Limits: 1 <= k <= min(V, 2048), V <= 2^31 - 1, hs >= 1, chunk >= 1,
  * ntok <= 2^31 - 1.
  */
 int vl_head_topk(const float *x, const void *w, int wdtype, int64_t ntok, int64_t V, int64_t hs,
                  int64_t k, uint32_t *ids, float *probs, int64_t chunk, void *scratch,
                  size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * vl_head_topk_tune -- vl_head_topk (same arguments, same results) that
+ * first times hipBLASLt's candidates for its product shape when that
+ * product runs in hipBLASLt and the shape is not yet tuned, as
+ * vl_head_kl_tune does (this call then waits for `stream`).
+ */
+int vl_head_topk_tune(const float *x, const void *w, int wdtype, int64_t ntok, int64_t V,
+                      int64_t hs, int64_t k, uint32_t *ids, float *probs, int64_t chunk,
+                      void *scratch, size_t scratch_bytes, hipStream_t stream);
 
 /* Static text naming a status code. */
 const char *vl_strerror(int status);

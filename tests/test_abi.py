@@ -31,7 +31,8 @@ def test_header_declares_the_calls():
          "vl_topk_renorm", "vl_slice_acc", "vl_head_scratch_bytes", "vl_head_kl",
          "vl_kl_slice_fwd", "vl_kl_slice_merge", "vl_kl_slice_bwd", "vl_strerror",
          "vl_split_workspace_bytes", "vl_ce_fwd_bwd_ws", "vl_kl_fwd_bwd_ws",
-         "vl_kl_fwd_bwd_noalloc", "vl_head_topk_scratch_bytes", "vl_head_topk"])
+         "vl_kl_fwd_bwd_noalloc", "vl_head_topk_scratch_bytes", "vl_head_topk",
+         "vl_head_kl_tune", "vl_head_topk_tune"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -170,8 +171,9 @@ def test_head_scratch_bytes(lib):
     assert f(32, (1 << 19) + 1, 256) == 0
 
 
-def test_head_host_checks(lib):
-    f = lib.vl_head_kl
+@pytest.mark.parametrize("name", ["vl_head_kl", "vl_head_kl_tune"])
+def test_head_host_checks(lib, name):
+    f = getattr(lib, name)
     ok = dict(x=P, w=P, wd=1, ids=P, probs=P, k=4, dx=P, loss=P, ntok=8, V=64, hs=16,
               total=8, gscale=1.0, chunk=4, scratch=P, sb=1 << 40, st=None)
 
@@ -311,7 +313,9 @@ def test_noalloc_host_checks(lib):
     assert f(ntok=0, logits=None) == VL_OK
 
 
-def test_head_topk_host_checks(lib):
+@pytest.mark.parametrize("call", ["vl_head_topk", "vl_head_topk_tune"])
+def test_head_topk_host_checks(lib, call):
+    fn = getattr(lib, call)
     n = lib.vl_head_topk_scratch_bytes(8, 1000, 64)
     assert n >= 8 * 1000 * 4 + 8 * 64 * 2 + (64 << 20)
     assert lib.vl_head_topk_scratch_bytes(0, 1000, 64) == 0
@@ -321,9 +325,8 @@ def test_head_topk_host_checks(lib):
         a = dict(x=P, w=P, wd=1, ntok=4, V=1000, hs=64, k=16, ids=P, probs=P, chunk=8,
                  scratch=P, sb=n, stream=None)
         a.update(kw)
-        return lib.vl_head_topk(a["x"], a["w"], a["wd"], a["ntok"], a["V"], a["hs"], a["k"],
-                                a["ids"], a["probs"], a["chunk"], a["scratch"], a["sb"],
-                                a["stream"])
+        return fn(a["x"], a["w"], a["wd"], a["ntok"], a["V"], a["hs"], a["k"], a["ids"],
+                  a["probs"], a["chunk"], a["scratch"], a["sb"], a["stream"])
     assert f(wd=0) == VL_EDTYPE
     assert f(k=0) == VL_EINVAL
     assert f(k=1001) == VL_EINVAL

@@ -165,6 +165,51 @@ def test_head_nan_weight_and_row(vl, hs):
     check(loss[keep], dx[keep], rl[keep], rdx[keep], "f16")
 
 
+@pytest.mark.parametrize("hs", [64, 20])
+def test_head_tune_then_plain(vl, hs):
+    """vl_head_kl_tune, then vl_head_kl twice on the same shape: all three
+    match the oracle, and the two plain calls, which run the tuned choice,
+    agree bit for bit.  hs = 20 puts both products in hipBLASLt, hs = 64
+    only the dx product."""
+    ntok, V, k, chunk = 40, 3000, 8, 40
+    c = gi.head_inputs(ntok, V, hs, k, 8400 + hs, DEV, torch.bfloat16)
+    total, gscale = ntok, 128.0
+    rl, rdx = oracle_for(c["x"], c["w"], c["ids"], c["probs"], total, gscale, "bf16")
+    dx = torch.full((ntok, hs), float("nan"), device=DEV)
+    loss = torch.full((ntok,), float("nan"), device=DEV)
+    scratch = torch.empty(vl.vl_head_scratch_bytes(chunk, V, hs), dtype=torch.uint8, device=DEV)
+    vl.vl_head_kl(c["x"], c["w"], c["ids"], c["probs"], dx, loss, total, gscale, chunk, scratch,
+                  tune=True)
+    torch.cuda.synchronize()
+    check(loss.cpu().numpy().astype(np.float64), dx.cpu().numpy().astype(np.float64), rl, rdx,
+          "bf16")
+    a = run_head(vl, c["x"], c["w"], c["ids"], c["probs"], total, gscale, chunk)
+    b = run_head(vl, c["x"], c["w"], c["ids"], c["probs"], total, gscale, chunk)
+    check(a[0], a[1], rl, rdx, "bf16")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_head_topk_tune(vl):
+    """vl_head_topk_tune on a shape whose product runs in hipBLASLt (hs not a
+    multiple of 8), on exact logits: the same ids and probabilities as the
+    plain call and the oracle's ids."""
+    ntok, V, hs, k = 30, 2000, 20, 16
+    x, w = dyadic_head(ntok, V, hs, 8500, "bf16")
+    scratch = torch.empty(vl.vl_head_topk_scratch_bytes(ntok, V, hs), dtype=torch.uint8,
+                          device=DEV)
+    out = []
+    for tune in (True, False):
+        ids = torch.empty((ntok, k), dtype=torch.int32, device=DEV)
+        probs = torch.empty((ntok, k), device=DEV)
+        vl.vl_head_topk(x, w, k, ids, probs, ntok, scratch, tune=tune)
+        torch.cuda.synchronize()
+        out.append((ids.cpu().numpy(), probs.cpu().numpy()))
+    assert np.array_equal(out[0][0], out[1][0]) and np.array_equal(out[0][1], out[1][1])
+    oi, _ = oracle.head_topk(x.cpu().numpy().astype(np.float64),
+                             w.float().cpu().numpy().astype(np.float64), k)
+    assert np.array_equal(out[0][0].view(np.uint32), oi)
+
+
 def run_head_topk(vl, x, w, k, chunk):
     ntok, hs = x.shape
     V = w.shape[0]

@@ -68,6 +68,8 @@ def _load():
     lib.vl_head_kl.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, i64, i64, i64, i64, f32, i64,
                                vp, ctypes.c_size_t, vp]
     lib.vl_head_kl.restype = i32
+    lib.vl_head_kl_tune.argtypes = lib.vl_head_kl.argtypes
+    lib.vl_head_kl_tune.restype = i32
     lib.vl_kl_slice_fwd.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp, i64, rp, vp]
     lib.vl_kl_slice_merge.argtypes = [vp, i64, vp, vp, i64, rp, vp]
     lib.vl_kl_slice_bwd.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp, i64, rp, f32, vp]
@@ -82,6 +84,8 @@ def _load():
     lib.vl_head_topk_scratch_bytes.restype = sz
     lib.vl_head_topk.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, vp, sz, vp]
     lib.vl_head_topk.restype = i32
+    lib.vl_head_topk_tune.argtypes = lib.vl_head_topk.argtypes
+    lib.vl_head_topk_tune.restype = i32
     lib.vl_strerror.argtypes = [i32]
     lib.vl_strerror.restype = ctypes.c_char_p
     for f in (lib.vl_ce_fwd_bwd, lib.vl_ce_fwd, lib.vl_ce_bwd, lib.vl_loss_mean,
@@ -291,11 +295,13 @@ def vl_head_scratch_bytes(chunk, V, hs):
     return int(_lib.vl_head_scratch_bytes(int(chunk), int(V), int(hs)))
 
 
-def vl_head_kl(x, w, ids, probs, dx, loss, total, gscale, chunk, scratch, stream=None):
+def vl_head_kl(x, w, ids, probs, dx, loss, total, gscale, chunk, scratch, stream=None,
+               tune=False):
     """Vocabulary head + distillation KL; see vl_head_kl in vl.h.  ``w`` is
     a torch.float16 or torch.bfloat16 [V][hs] tensor; ``scratch`` a uint8
     device tensor of at least vl_head_scratch_bytes(min(chunk, ntok), V, hs)
-    bytes."""
+    bytes.  ``tune=True`` calls vl_head_kl_tune instead (times hipBLASLt's
+    candidates for shapes not yet tuned; the host waits)."""
     ntok, hs = x.shape
     V = w.shape[0]
     k = ids.shape[1] if ids.dim() == 2 else 0
@@ -303,7 +309,9 @@ def vl_head_kl(x, w, ids, probs, dx, loss, total, gscale, chunk, scratch, stream
     if wd is None:
         raise TypeError(f"w must be float16 or bfloat16, got {w.dtype}")
     with torch.cuda.device(x.device):
-        _check(_lib.vl_head_kl(
+        fn, name = (_lib.vl_head_kl_tune, "vl_head_kl_tune") if tune else (_lib.vl_head_kl,
+                                                                            "vl_head_kl")
+        _check(fn(
             _dev(x, "x", (torch.float32,)), _dev(w, "w", None, (V, hs)), wd,
             _dev(ids, "ids", _INT_IDS, (ntok, k)),
             _dev(probs, "probs", (torch.float32,), (ntok, k)), k,
@@ -311,7 +319,7 @@ def vl_head_kl(x, w, ids, probs, dx, loss, total, gscale, chunk, scratch, stream
             _dev(loss, "loss", (torch.float32,), (ntok,)),
             ntok, V, hs, int(total), float(gscale), int(chunk),
             _dev(scratch, "scratch", (torch.uint8,)), scratch.numel(),
-            _stream(x, stream)), "vl_head_kl")
+            _stream(x, stream)), name)
 
 
 def vl_head_topk_scratch_bytes(chunk, V, hs):
@@ -319,24 +327,26 @@ def vl_head_topk_scratch_bytes(chunk, V, hs):
     return int(_lib.vl_head_topk_scratch_bytes(int(chunk), int(V), int(hs)))
 
 
-def vl_head_topk(x, w, k, ids, probs, chunk, scratch, stream=None):
+def vl_head_topk(x, w, k, ids, probs, chunk, scratch, stream=None, tune=False):
     """Teacher-side vocabulary head: top-k ids and renormalised
     probabilities of half(x) . w^T; see vl_head_topk in vl.h.  ``w`` is a
     torch.float16 or torch.bfloat16 [V][hs] tensor; ``scratch`` a uint8
     device tensor of at least vl_head_topk_scratch_bytes(min(chunk, ntok),
-    V, hs) bytes."""
+    V, hs) bytes.  ``tune=True`` calls vl_head_topk_tune instead."""
     ntok, hs = x.shape
     V = w.shape[0]
     wd = {torch.float16: VL_F16, torch.bfloat16: VL_BF16}.get(w.dtype)
     if wd is None:
         raise TypeError(f"w must be float16 or bfloat16, got {w.dtype}")
     with torch.cuda.device(x.device):
-        _check(_lib.vl_head_topk(
+        fn, name = ((_lib.vl_head_topk_tune, "vl_head_topk_tune") if tune
+                    else (_lib.vl_head_topk, "vl_head_topk"))
+        _check(fn(
             _dev(x, "x", (torch.float32,)), _dev(w, "w", None, (V, hs)), wd, ntok, V, hs,
             int(k), _dev(ids, "ids", _INT_IDS, (ntok, k)),
             _dev(probs, "probs", (torch.float32,), (ntok, k)), int(chunk),
             _dev(scratch, "scratch", (torch.uint8,)), scratch.numel(),
-            _stream(x, stream)), "vl_head_topk")
+            _stream(x, stream)), name)
 
 
 def _slice_rows(t: torch.Tensor, name: str):

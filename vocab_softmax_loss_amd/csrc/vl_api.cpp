@@ -305,10 +305,14 @@ size_t vl_head_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
     return vl::head_scratch_bytes(chunk, V, hs);
 }
 
-int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
-               const float *probs, int64_t k, float *dx, float *loss, int64_t ntok, int64_t V,
-               int64_t hs, int64_t total, float gscale, int64_t chunk, void *scratch,
-               size_t scratch_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+int head_kl_call(const float *x, const void *w, int wdtype, const uint32_t *ids,
+                 const float *probs, int64_t k, float *dx, float *loss, int64_t ntok, int64_t V,
+                 int64_t hs, int64_t total, float gscale, int64_t chunk, void *scratch,
+                 size_t scratch_bytes, bool tune, hipStream_t stream)
 {
     if (wdtype != VL_BF16 && wdtype != VL_F16)
         return VL_EDTYPE;
@@ -325,8 +329,30 @@ int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
     if (scratch_bytes < vl::head_scratch_bytes(c, V, hs))
         return VL_EINVAL;
     vl::HeadArgs a{x, w, wdtype, ids, probs, dx, loss, ntok, V, hs, k, total, c, gscale,
-                   scratch};
+                   scratch, tune};
     return vl::head_kl(a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int vl_head_kl(const float *x, const void *w, int wdtype, const uint32_t *ids,
+               const float *probs, int64_t k, float *dx, float *loss, int64_t ntok, int64_t V,
+               int64_t hs, int64_t total, float gscale, int64_t chunk, void *scratch,
+               size_t scratch_bytes, hipStream_t stream)
+{
+    return head_kl_call(x, w, wdtype, ids, probs, k, dx, loss, ntok, V, hs, total, gscale, chunk,
+                        scratch, scratch_bytes, false, stream);
+}
+
+int vl_head_kl_tune(const float *x, const void *w, int wdtype, const uint32_t *ids,
+                    const float *probs, int64_t k, float *dx, float *loss, int64_t ntok,
+                    int64_t V, int64_t hs, int64_t total, float gscale, int64_t chunk,
+                    void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    return head_kl_call(x, w, wdtype, ids, probs, k, dx, loss, ntok, V, hs, total, gscale, chunk,
+                        scratch, scratch_bytes, true, stream);
 }
 
 size_t vl_head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
@@ -338,9 +364,13 @@ size_t vl_head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs)
     return vl::head_topk_scratch_bytes(chunk, V, hs);
 }
 
-int vl_head_topk(const float *x, const void *w, int wdtype, int64_t ntok, int64_t V, int64_t hs,
-                 int64_t k, uint32_t *ids, float *probs, int64_t chunk, void *scratch,
-                 size_t scratch_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+int head_topk_call(const float *x, const void *w, int wdtype, int64_t ntok, int64_t V,
+                   int64_t hs, int64_t k, uint32_t *ids, float *probs, int64_t chunk,
+                   void *scratch, size_t scratch_bytes, bool tune, hipStream_t stream)
 {
     if (wdtype != VL_BF16 && wdtype != VL_F16)
         return VL_EDTYPE;
@@ -356,8 +386,28 @@ int vl_head_topk(const float *x, const void *w, int wdtype, int64_t ntok, int64_
     const int64_t c = chunk < ntok ? chunk : ntok;
     if (scratch_bytes < vl::head_topk_scratch_bytes(c, V, hs))
         return VL_EINVAL;
-    vl::HeadTopkArgs a{x, w, wdtype, ntok, V, hs, k, c, ids, probs, scratch};
+    vl::HeadTopkArgs a{x, w, wdtype, ntok, V, hs, k, c, ids, probs, scratch, tune};
     return vl::head_topk(a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int vl_head_topk(const float *x, const void *w, int wdtype, int64_t ntok, int64_t V, int64_t hs,
+                 int64_t k, uint32_t *ids, float *probs, int64_t chunk, void *scratch,
+                 size_t scratch_bytes, hipStream_t stream)
+{
+    return head_topk_call(x, w, wdtype, ntok, V, hs, k, ids, probs, chunk, scratch,
+                          scratch_bytes, false, stream);
+}
+
+int vl_head_topk_tune(const float *x, const void *w, int wdtype, int64_t ntok, int64_t V,
+                      int64_t hs, int64_t k, uint32_t *ids, float *probs, int64_t chunk,
+                      void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    return head_topk_call(x, w, wdtype, ntok, V, hs, k, ids, probs, chunk, scratch,
+                          scratch_bytes, true, stream);
 }
 
 int vl_kl_fwd_bwd(void *logits, int dtype, const uint32_t *ids, const float *probs, int64_t k,

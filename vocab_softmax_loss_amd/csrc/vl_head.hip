@@ -371,9 +371,11 @@ hipblasLtHandle_t lt_handle()
 // The algorithm each GEMM shape runs with, per device.  hipBLASLt's first
 // heuristic choice is not its fastest for these shapes (the logits product
 // at 4096 x 151936 x 1024 bf16: 1.73 ms against 1.35 ms for the best of its
-// first 16), so the first call with a shape times the candidates once, on
-// the caller's stream, and later calls reuse the fastest.  Under stream
-// capture nothing is timed and the first choice runs.
+// first 16).  A tuning call (tune set) with a shape not yet timed times the
+// candidates once on the caller's stream, waiting for them, and caches the
+// fastest; every other call runs the cached choice, or hipBLASLt's first
+// choice when there is none, and never waits.  Under stream capture nothing
+// is timed.
 struct AlgoKey {
     int dev, ta, tb, ht;
     int64_t m, n, k;
@@ -427,7 +429,7 @@ bool finish(bool ok, hipblasLtMatmulDesc_t desc, hipblasLtMatrixLayout_t la,
 bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int64_t m,
           int64_t n, int64_t k, float alpha, const void *A, int64_t lda, const void *B,
           int64_t ldb, float *C, int64_t ldc, hipDataType ht, void *ws, size_t ws_bytes,
-          hipStream_t st)
+          bool tune, hipStream_t st)
 {
     hipblasLtMatmulDesc_t desc = nullptr;
     hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
@@ -469,8 +471,8 @@ bool gemm(hipblasLtHandle_t h, hipblasOperation_t ta, hipblasOperation_t tb, int
     if (!ok)
         return finish(false, desc, la, lb, lc, pref);
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone ||
-        found == 1)
+    if (!tune || hipStreamIsCapturing(st, &cap) != hipSuccess ||
+        cap != hipStreamCaptureStatusNone || found == 1)
         return finish(run(res[0].algo), desc, la, lb, lc, pref);
     // Time each candidate: one untimed run, then two timed ones.
     hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -670,7 +672,7 @@ int head_topk(const HeadTopkArgs &a, hipStream_t st)
             if (to_half(bf, a.x + r0 * a.hs, act, rows * a.hs, st) != hipSuccess)
                 return VL_ELAUNCH;
             if (!gemm(h, HIPBLAS_OP_T, HIPBLAS_OP_N, a.V, rows, a.hs, 1.f, a.w, a.hs, act, a.hs,
-                      logits, a.V, ht, ws, kHeadWorkspace, st))
+                      logits, a.V, ht, ws, kHeadWorkspace, a.tune, st))
                 return VL_ELAUNCH;
         }
         TopkArgs t{logits, rows, a.V, a.k, a.ids + r0 * a.k, a.probs + r0 * a.k};
@@ -744,7 +746,7 @@ int head_kl(const HeadArgs &a, hipStream_t st)
                 return VL_ELAUNCH;
             // logits (row-major rows x V) = column-major V x rows = W . act^T
             if (!gemm(h, HIPBLAS_OP_T, HIPBLAS_OP_N, a.V, rows, a.hs, 1.f, a.w, a.hs, act, a.hs,
-                      logits, a.V, ht, ws, kHeadWorkspace, st))
+                      logits, a.V, ht, ws, kHeadWorkspace, a.tune, st))
                 return VL_ELAUNCH;
             RowArgs r{};
             r.logits = logits;
@@ -762,7 +764,7 @@ int head_kl(const HeadArgs &a, hipStream_t st)
         }
         // dx (row-major rows x hs) = column-major hs x rows = W^T . dl^T
         if (!gemm(h, HIPBLAS_OP_N, HIPBLAS_OP_N, a.hs, rows, a.V, 1.f / a.gscale, a.w, a.hs, dl,
-                  a.V, a.dx + r0 * a.hs, a.hs, ht, ws, kHeadWorkspace, st))
+                  a.V, a.dx + r0 * a.hs, a.hs, ht, ws, kHeadWorkspace, a.tune, st))
             return VL_ELAUNCH;
     }
     return VL_OK;

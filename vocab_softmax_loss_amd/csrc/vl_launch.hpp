@@ -318,6 +318,7 @@ struct HeadArgs {
     int64_t ntok, V, hs, k, total, chunk;
     float gscale;
     void *scratch;          // head_scratch_bytes(min(chunk, ntok), V, hs) bytes
+    bool tune;              // time hipBLASLt's candidates for an untimed shape
 };
 
 // Scratch bytes of one head call with `chunk` rows at a time.
@@ -334,6 +335,7 @@ struct HeadTopkArgs {
     uint32_t *ids;          // [ntok][k]
     float *probs;           // [ntok][k]
     void *scratch;          // head_topk_scratch_bytes(min(chunk, ntok), V, hs) bytes
+    bool tune;              // time hipBLASLt's candidates for an untimed shape
 };
 size_t head_topk_scratch_bytes(int64_t chunk, int64_t V, int64_t hs);
 int head_topk(const HeadTopkArgs &a, hipStream_t stream);
