@@ -148,12 +148,45 @@ def cpu_baseline(h, rng, scale, rows: int, rows_1core: int):
                                       f"{dt1:.2f} s wall-clock on 1 thread"}}
 
 
+def workload_cpu_baseline(run, ntok, rows, rows_1core, what):
+    """The float64 oracle over the first rows of one configuration, timed on
+    every thread the OpenMP runtime uses and on one thread.  `run(n)` runs
+    the oracle's stages of the configuration on the first n rows (inputs
+    copied to the host before the GPU calls overwrite them)."""
+    import oracle
+    run(2)  # load the library outside the timing
+    threads = oracle.threads()
+    t0 = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t0
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        run(rows_1core)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
+    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of the {ntok} rows ({what}), float64, {dt:.2f} s "
+                      f"wall-clock on {threads} threads",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_core": {"value": rows_1core / dt1, "unit": "rows/s", "cores": 1,
+                            "sample": f"first {rows_1core} rows, {dt1:.2f} s wall-clock on "
+                                      f"1 thread"}}
+
+
 def other_workload(name, dev):
-    """(calls, bytes per call, ntok, config) of one full-size configuration.
-    Each call is (kernel name, function)."""
+    """(calls, bytes per call, ntok, config, cpu) of one full-size
+    configuration.  Each call is (kernel name, function); cpu is None or a
+    function of no arguments that times the oracle on a sample of the same
+    inputs (host copies taken here, before any call)."""
+    import numpy as np
     import torch
     import vocab_softmax_loss_amd as vl
     from gen import inputs as gi
+    from gen.inputs import to_host_bytes
+
+    cpu = None
 
     if name == "ce_lm":
         c = gi.ce_lm(dev)
@@ -164,6 +197,13 @@ def other_workload(name, dev):
                                                  scale=c["scale"]))]
         nbytes = {"ce": n_in * 2 * V * 4 + (ntok - n_in) * V * 4 + ntok * 8}
         cfg = {"workload": gi.CE_LM.name, "ntok": ntok, "V": V, "dtype": "f32"}
+        hx, hl = to_host_bytes(c["logits"]), to_host_bytes(c["labels"])
+
+        def cpu():
+            import oracle
+            return workload_cpu_baseline(
+                lambda n: oracle.ce(hx[:n], hl[:n], rng=c["rng"], scale=c["scale"]),
+                ntok, ntok, ntok, "CE loss and gradient")
     elif name == "ce_split":
         # the same configuration through the two-pass calls: forward only,
         # backward from the saved lse, then the mean loss on the device
@@ -191,6 +231,12 @@ def other_workload(name, dev):
         calls = [("topk", lambda: vl.vl_topk_renorm(t, k, ids, probs))]
         nbytes = {"topk": ntok * V * 4 + ntok * k * 8}
         cfg = {"workload": gi.TOPK_ZIPF.name, "ntok": ntok, "V": V, "k": k, "dtype": "f32"}
+        ht = to_host_bytes(t)
+
+        def cpu():
+            import oracle
+            return workload_cpu_baseline(lambda n: oracle.topk(ht[:n], k), ntok, ntok, 512,
+                                         "top-k and renormalised probabilities")
     elif name in ("kl_large", "kl_large_unsplit"):
         c = gi.kl_large(dev)
         x = c["logits"]
@@ -214,6 +260,14 @@ def other_workload(name, dev):
         nbytes = {"kl": ntok * 2 * V * 4 + ntok * k * 8 + ntok * 4}
         cfg = {"workload": gi.KL_LARGE.name, "ntok": ntok, "V": V, "k": k, "dtype": "f32",
                "bytes_model": model}
+        hx = to_host_bytes(x[:4096])
+        hi, hp = to_host_bytes(c["ids"][:4096]), to_host_bytes(c["probs"][:4096])
+
+        def cpu():
+            import oracle
+            return workload_cpu_baseline(
+                lambda n: oracle.kl(hx[:n], hi[:n], hp[:n], coef=c["coef"]), ntok, 4096, 512,
+                "KL loss and gradient")
     elif name == "kl_bf16":
         c = gi.kl_bf16_sliced(dev)
         x, t, k = c["logits"], c["teacher"], c["k"]
@@ -232,6 +286,19 @@ def other_workload(name, dev):
                   "acc": 3 * ntok * hs * 4}
         cfg = {"workload": gi.KL_BF16.name, "ntok": ntok, "V": V, "k": k, "dtype": "bf16",
                "bytes_model": "KL 1R+1W"}
+        hx, ht = to_host_bytes(x[:1024]), to_host_bytes(t[:1024])
+        h0, h1 = to_host_bytes(c["dh0"][:1024]), to_host_bytes(c["dh1"][:1024])
+
+        def cpu():
+            import oracle
+
+            def run(n):
+                oi, op = oracle.topk(ht[:n], k)
+                oracle.kl(hx[:n], oi, op.astype(np.float32), coef=c["coef"])
+                oracle.acc(h0[:n], h1[:n])
+            return workload_cpu_baseline(run, ntok, 1024, 64,
+                                         "teacher top-k, KL loss and gradient, slice "
+                                         "accumulate of the row's 1024 values")
     elif name == "kl_sliced":
         # the same bf16 workload as two vocabulary slices of 75968, each its
         # own [ntok][75968] buffer: statistics of each slice, the merge, the
@@ -319,7 +386,7 @@ def other_workload(name, dev):
                "bytes": COPY_CALIB_BYTES, "dtype": "f32"}
     else:
         raise SystemExit(f"unknown workload {name}")
-    return calls, nbytes, ntok, cfg
+    return calls, nbytes, ntok, cfg, cpu
 
 
 def kernel_sources_sha256():
@@ -455,7 +522,7 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     if args.workload != "step":
-        calls, nbytes, ntok, cfg = other_workload(args.workload, dev)
+        calls, nbytes, ntok, cfg, cpu = other_workload(args.workload, dev)
         per, seq_ms = time_calls(calls, args.steps, args.warmup)
         kernels = kernel_table(per, nbytes, ntok)
         dom = max(per, key=per.get)
@@ -475,7 +542,8 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(seq_ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": cfg["dtype"], "data": "synthetic", "config": cfg,
-            "roofline": roof, "kernels": kernels, "cpu_baseline": None}), flush=True)
+            "roofline": roof, "kernels": kernels,
+            "cpu_baseline": None if (cpu is None or args.no_cpu) else cpu()}), flush=True)
         return
     x = make_inputs(dev)
     host = None if args.no_cpu else host_copies(x)
