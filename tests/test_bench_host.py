@@ -85,3 +85,27 @@ def test_kernel_table_rates(ms, nbytes):
     else:
         assert t["GB/s"] == round(nbytes / (ms * 1e-3) / 1e9, 1)
         assert t["frac"] == round(t["GB/s"] / bench.HBM_PEAK_GBS, 4)
+
+
+def test_workload_cpu_baseline_times_the_oracle_on_all_threads_and_one():
+    """The per-configuration CPU baseline runs the given oracle stages on
+    every OpenMP thread and then on one, restores the thread count, and
+    reports rows/s for each with the samples it timed."""
+    import numpy as np
+    import oracle
+
+    x = np.random.default_rng(7).normal(size=(64, 256)).astype(np.float32)
+    lab = np.arange(64, dtype=np.uint32) % 256
+    seen = []
+
+    def run(n):
+        seen.append((n, oracle.threads()))
+        oracle.ce(x[:n], lab[:n])
+
+    before = oracle.threads()
+    c = bench.workload_cpu_baseline(run, 64, 64, 16, "CE")
+    assert oracle.threads() == before
+    assert seen[0] == (2, before) and seen[1] == (64, before) and seen[2] == (16, 1)
+    assert c["kind"] == "oracle" and c["unit"] == "rows/s" and c["cores"] == before
+    assert c["value"] > 0 and c["single_core"]["value"] > 0 and c["single_core"]["cores"] == 1
+    assert "first 64 of the 64 rows (CE)" in c["sample"] and c["cpu_model"]
