@@ -145,8 +145,9 @@ namespace {
 // Rows the single-CU kernels cannot hold on chip go to the split kernels:
 // float32 rows past 8192 16-byte vectors (32768 values), bf16 rows past the
 // 19456 vectors (155648 values) a 1024-thread block holds in registers.  The
-// bf16 rows in between run as fast whole in one block's registers (16384 x
-// 151936: 2.06 ms either way) and need no exchange.
+// bf16 rows in between run faster whole in one block's registers (16384 x
+// 151936: 1.98 ms, against 2.03-2.10 ms split over 4 to 8 workgroups) and
+// need no exchange.
 // A split is one cooperative launch, which a stream under capture does not
 // take: captured calls run the rows whole (the same results within rounding).
 bool use_split(int dtype, const vl::RowArgs &a, int &S, hipStream_t stream)
